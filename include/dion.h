@@ -1,0 +1,158 @@
+/*
+ * libdion — one Dion / Orth-Dion optimizer step on an AMD MI355X (gfx950).
+ *
+ * The step is the one written out on the "Orth-Dion" documentation page
+ * (junaidaliop.github.io, zij/math/orthdion): its equation block and the
+ * symbol list below it.  For a weight matrix X (m x n) with gradient G,
+ * error-feedback residual R (both m x n) and warm start V (n x r):
+ *
+ *   M    = G + R                       buffer
+ *   U    = orth(M V)                   one warm-started power-iteration step
+ *   W    = M^T U                       right factor
+ *   Vbar = orth(W)                     Orth-Dion
+ *        = W diag(1 / ||w_j||_2)       Dion (the page's closing remark: column
+ *                                      normalization in place of orth)
+ *   X   <- X - eta U Vbar^T
+ *   R   <- beta (M - U W^T)            (U^T M = W^T, so W is reused)
+ *   V   <- Vbar                        warm start of the next step
+ *
+ * orth(A) is the Q factor of the thin QR factorization A = Q T whose upper
+ * triangular T has a positive diagonal; that choice makes Q unique for a
+ * full-rank A.  The library computes it by CholeskyQR applied twice
+ * (float32 Gram products on the matrix cores, float64 Cholesky and triangular
+ * inverse).
+ *
+ * Conventions for every entry point:
+ *   - All functions are extern "C"; no C++ exception crosses the boundary.
+ *   - Matrices are dense row-major (C order) with no padding: element (i, j)
+ *     of an a x b matrix is at p[i * b + j].  X, R, V are float32; G is
+ *     float32 or bfloat16 (raw 16-bit patterns), chosen by g_dtype.
+ *   - All pointers passed as matrices or workspace are DEVICE pointers on the
+ *     current HIP device.  The caller owns them.  X, R and V are updated in
+ *     place; G is only read.  X, G, R, V and the workspace must not overlap.
+ *     They need natural alignment (4 bytes; 2 for bfloat16 G); 16-byte
+ *     aligned pointers with a column count divisible by 4 take the vector
+ *     load path.
+ *   - stream is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued: the calls return before the GPU finishes and never
+ *     synchronize the host, except dion_status.  Buffers must stay valid
+ *     until the enqueued work completes.
+ *   - Argument errors are reported synchronously, before any HIP call is
+ *     made, and leave every buffer untouched.
+ *   - A numerical breakdown (orth of a numerically rank-deficient or
+ *     non-finite factor; a zero or non-finite column norm for Dion) can only
+ *     be seen on the device.  It is recorded in a status word inside the
+ *     workspace, and every later kernel of that matrix skips its writes, so
+ *     X, R and V of that matrix keep their previous contents bit for bit.
+ *     Read it with dion_status.
+ */
+#ifndef LIBDION_DION_H_
+#define LIBDION_DION_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define DION_OK               0
+#define DION_ERR_INVALID_ARG (-1)  /* null pointer, bad size, rank, variant, dtype, non-finite eta/beta */
+#define DION_ERR_WORKSPACE   (-2)  /* workspace missing or smaller than required */
+#define DION_ERR_HIP         (-3)  /* a HIP runtime call or kernel launch failed */
+#define DION_ERR_BREAKDOWN   (-4)  /* (dion_status only) numerical breakdown on the device */
+
+/* Right-factor rule: equation 4 of the Orth-Dion page, or Dion's column
+ * normalization. */
+#define DION_VARIANT_DION 0
+#define DION_VARIANT_ORTH 1
+
+/* Element type of G. */
+#define DION_DTYPE_F32  0
+#define DION_DTYPE_BF16 1
+
+/* Per-matrix breakdown flags reported by dion_status (0 = step applied). */
+#define DION_STATUS_ORTH_P   1   /* orth(M V) failed */
+#define DION_STATUS_ORTH_W   2   /* orth(W) failed (Orth-Dion) */
+#define DION_STATUS_COLNORM  4   /* zero or non-finite column norm (Dion) */
+
+/* Upper bounds accepted by the library. */
+#define DION_MAX_DIM   (1 << 20)      /* m, n */
+#define DION_MAX_RANK  4096           /* r */
+
+/* One matrix of a grouped step.  Device pointers, row-major, see above. */
+typedef struct dion_matrix {
+    float*       X;   /* m x n, updated in place */
+    const void*  G;   /* m x n, float32 or bfloat16 per g_dtype, read only */
+    float*       R;   /* m x n, updated in place */
+    float*       V;   /* n x r, warm start in, Vbar out */
+    int64_t      m, n, r;
+} dion_matrix;
+
+/* Opaque handle for a grouped step over a fixed list of matrices. */
+typedef struct dion_plan dion_plan;
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int dion_version(void);
+
+/* Static string for a return code (never NULL). */
+const char* dion_error_string(int code);
+
+/* Workspace bytes one dion_step call on an m x n matrix of rank r needs.
+ * Returns 0 when the arguments are invalid. */
+size_t dion_workspace_size(int64_t m, int64_t n, int64_t r, int variant, int g_dtype);
+
+/* One step on one matrix (the equations at the top of this header).
+ *   X, G, R, V: device pointers (see conventions); m, n >= 1; 1 <= r <= min(m, n).
+ *   eta: learning rate, beta: error-feedback coefficient (finite floats).
+ *   variant: DION_VARIANT_*; g_dtype: DION_DTYPE_*.
+ *   workspace: device buffer of at least dion_workspace_size(...) bytes,
+ *   16-byte aligned, owned by the caller; its contents need not be preserved
+ *   between calls except for the status word read by dion_status.
+ * Returns DION_OK once the work is enqueued, or an error code (nothing
+ * enqueued for argument errors). */
+int dion_step(float* X, const void* G, float* R, float* V,
+              int64_t m, int64_t n, int64_t r, float eta, float beta,
+              int variant, int g_dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Grouped step: the same update applied to each matrix of a list (for
+ * example all weight matrices of a model) with a handful of kernel launches
+ * for the whole list.  Matrices may have different shapes.  Equivalent to a
+ * dion_step call per matrix.  The matrix list is copied; the call keeps an
+ * internal cache of plans keyed by the list, so repeating the same list
+ * costs no host-side setup. */
+size_t dion_workspace_size_batched(const dion_matrix* mats, int count,
+                                   int variant, int g_dtype);
+int dion_step_batched(const dion_matrix* mats, int count, float eta, float beta,
+                      int variant, int g_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Explicit plan for a grouped step (what dion_step_batched caches).
+ * dion_plan_create validates the list and builds the schedule on the host;
+ * it allocates pinned host memory for the matrix table (no device memory).
+ * dion_plan_step enqueues one grouped step: an asynchronous copy of the
+ * table into the workspace, then the kernels.  dion_plan_destroy waits for
+ * the last table copy of this plan to finish, then frees it. */
+int    dion_plan_create(const dion_matrix* mats, int count, int variant,
+                        int g_dtype, dion_plan** plan_out);
+size_t dion_plan_workspace_size(const dion_plan* plan);
+int    dion_plan_count(const dion_plan* plan);
+int    dion_plan_step(dion_plan* plan, float eta, float beta,
+                      void* workspace, size_t workspace_bytes, void* stream);
+void   dion_plan_destroy(dion_plan* plan);
+
+/* Breakdown check: waits for `stream`, then reads the status words of the
+ * last step enqueued on `workspace` (count = 1 for dion_step, the list
+ * length for a grouped step).  per_matrix (optional, count ints) receives
+ * each matrix's DION_STATUS_* flags, in the caller's list order.
+ * Returns DION_OK, DION_ERR_BREAKDOWN if any matrix broke down, or an
+ * argument / HIP error. */
+int dion_status(const void* workspace, int count, void* stream, int* per_matrix);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBDION_DION_H_ */

@@ -1,0 +1,318 @@
+// Device building blocks of libdion's gfx950 kernels: work lookup for
+// grouped launches, XCD-aware block order, LDS tile loaders, and the float32
+// MFMA main loop.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dion_types.h"
+
+namespace dion {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;   // every kernel runs 4 wavefronts of 64
+
+// Workgroups of a launch are handed to the 8 XCDs round-robin (block b goes
+// to XCD b % 8).  Renumber them so each XCD owns one contiguous range of
+// logical work items; neighbouring tiles share operands, and each XCD has
+// its own L2.
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int q = nb >> 3, rem = nb & 7;
+  const int x = b & 7, i = b >> 3;
+  return x * q + (x < rem ? x : rem) + i;
+}
+
+// Find the matrix and the local work item of logical item t.
+__device__ __forceinline__ void locate(const Launch& L, int t, MatDesc& d,
+                                       ClassInfo& ci, int& local) {
+  ci = L.cls[0];
+#pragma unroll
+  for (int c = 1; c < kMaxClasses; ++c)
+    if (c < L.nclass && t >= L.cls[c].base) ci = L.cls[c];
+  const int rel = t - ci.base;
+  const int mi = rel / ci.tiles;
+  local = rel - mi * ci.tiles;
+  d = L.table ? L.table[ci.first + mi] : L.inl;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Element sources.  ld4 reads 4 consecutive elements (16-byte aligned for
+// float32), ld1 one element; both return float32.
+struct SrcF32 {
+  const float* p;
+  __device__ __forceinline__ f32x4 ld4(int64_t o) const {
+    return *reinterpret_cast<const f32x4*>(p + o);
+  }
+  __device__ __forceinline__ float ld1(int64_t o) const { return p[o]; }
+};
+
+// The buffer M = G + R, formed on the fly (one float32 rounding, the same
+// everywhere it is formed).
+template <typename GT> struct SrcM;
+template <> struct SrcM<float> {
+  const float* g;
+  const float* r;
+  __device__ __forceinline__ f32x4 ld4(int64_t o) const {
+    return *reinterpret_cast<const f32x4*>(g + o) +
+           *reinterpret_cast<const f32x4*>(r + o);
+  }
+  __device__ __forceinline__ float ld1(int64_t o) const { return g[o] + r[o]; }
+};
+template <> struct SrcM<uint16_t> {
+  const uint16_t* g;
+  const float* r;
+  __device__ __forceinline__ f32x4 ld4(int64_t o) const {
+    const uint2 u = *reinterpret_cast<const uint2*>(g + o);
+    f32x4 a;
+    a[0] = __uint_as_float(u.x << 16);
+    a[1] = __uint_as_float(u.x & 0xffff0000u);
+    a[2] = __uint_as_float(u.y << 16);
+    a[3] = __uint_as_float(u.y & 0xffff0000u);
+    return a + *reinterpret_cast<const f32x4*>(r + o);
+  }
+  __device__ __forceinline__ float ld1(int64_t o) const {
+    return bf16_to_f32(g[o]) + r[o];
+  }
+};
+
+// float64 source rounded to float32 (the triangular inverse).
+struct SrcF64 {
+  const double* p;
+  __device__ __forceinline__ f32x4 ld4(int64_t o) const {
+    const double2 a = *reinterpret_cast<const double2*>(p + o);
+    const double2 b = *reinterpret_cast<const double2*>(p + o + 2);
+    f32x4 v;
+    v[0] = static_cast<float>(a.x);
+    v[1] = static_cast<float>(a.y);
+    v[2] = static_cast<float>(b.x);
+    v[3] = static_cast<float>(b.y);
+    return v;
+  }
+  __device__ __forceinline__ float ld1(int64_t o) const {
+    return static_cast<float>(p[o]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// LDS tile layout: for an operand tile of BX rows (the output dimension it
+// feeds) by BK reduction steps, LDS holds float4 cells cell[kg][x] =
+// (e(x,4kg), e(x,4kg+1), e(x,4kg+2), e(x,4kg+3)), row pitch BX + PAD cells.
+// A wavefront reads a fragment with one ds_read_b128 per lane: lane l takes
+// cell[2q + l/32][x0 + l%32], i.e. 4 reduction steps at once; the MFMA loop
+// then pairs lanes 0-31 (k = 8q + c) with lanes 32-63 (k = 8q + 4 + c).
+// Both operands use the same k order, so the product is unchanged.
+template <int BX, int BK> struct TileShape {
+  static constexpr int PAD = 64 / BK;          // conflict-free cell stores
+  static constexpr int PITCH = BX + PAD;       // float4 cells per kg row
+  static constexpr int CELLS = (BK / 4) * PITCH;
+};
+
+// Loader for a source whose reduction index is contiguous:
+// element (x, k) = src[x * ld + k].  Each row of the tile is read as BK/4
+// consecutive float4 (full 128-byte lines for BK = 32).
+// TRI: element is zero when k > x (reading the transpose of a lower
+// triangle).
+template <int BX, int BK, bool VEC, bool TRI, class Src>
+struct LoadKC {
+  static constexpr int KQ = BK / 4;
+  static constexpr int NV = BX * KQ / kThreads;
+  static_assert(NV >= 1 && BX * KQ % kThreads == 0, "tile too small");
+  Src src;
+  int64_t ld;
+  int x0, xmax, kmax;
+  f32x4 v[NV];
+
+  __device__ __forceinline__ LoadKC(Src s, int64_t ld_, int x0_, int xmax_, int kmax_)
+      : src(s), ld(ld_), x0(x0_), xmax(xmax_), kmax(kmax_) {}
+
+  __device__ __forceinline__ void load(int k0) {
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      const int kq = idx % KQ, x = idx / KQ;
+      const int gx = x0 + x, gk = k0 + 4 * kq;
+      const int64_t o = static_cast<int64_t>(gx) * ld + gk;
+      if (VEC && gx < xmax && gk + 3 < kmax && (!TRI || gk + 3 <= gx)) {
+        v[s] = src.ld4(o);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool ok = gx < xmax && gk + c < kmax && (!TRI || gk + c <= gx);
+          v[s][c] = ok ? src.ld1(o + c) : 0.0f;
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(f32x4* lds) const {
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      const int kq = idx % KQ, x = idx / KQ;
+      lds[kq * TileShape<BX, BK>::PITCH + x] = v[s];
+    }
+  }
+};
+
+// Loader for a source whose output index is contiguous:
+// element (x, k) = src[k * ld + x].  Each thread reads a 4 (k) x 4 (x)
+// block as four float4 row pieces and transposes it in registers.
+template <int BX, int BK, bool VEC, class Src>
+struct LoadXC {
+  static constexpr int XQ = BX / 4;
+  static constexpr int NB = XQ * (BK / 4);
+  static constexpr int NPT = (NB + kThreads - 1) / kThreads;
+  Src src;
+  int64_t ld;
+  int x0, xmax, kmax;
+  f32x4 v[NPT][4];
+
+  __device__ __forceinline__ LoadXC(Src s, int64_t ld_, int x0_, int xmax_, int kmax_)
+      : src(s), ld(ld_), x0(x0_), xmax(xmax_), kmax(kmax_) {}
+
+  __device__ __forceinline__ void load(int k0) {
+#pragma unroll
+    for (int s = 0; s < NPT; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      if (NB % kThreads != 0 && idx >= NB) continue;
+      const int xq = idx % XQ, kg = idx / XQ;
+      const int gx = x0 + 4 * xq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gk = k0 + 4 * kg + j;
+        const int64_t o = static_cast<int64_t>(gk) * ld + gx;
+        if (VEC && gk < kmax && gx + 3 < xmax) {
+          v[s][j] = src.ld4(o);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            v[s][j][c] = (gk < kmax && gx + c < xmax) ? src.ld1(o + c) : 0.0f;
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(f32x4* lds) const {
+#pragma unroll
+    for (int s = 0; s < NPT; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      if (NB % kThreads != 0 && idx >= NB) continue;
+      const int xq = idx % XQ, kg = idx / XQ;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        f32x4 t;
+        t[0] = v[s][0][c];
+        t[1] = v[s][1][c];
+        t[2] = v[s][2][c];
+        t[3] = v[s][3][c];
+        lds[kg * TileShape<BX, BK>::PITCH + 4 * xq + c] = t;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// float32 MFMA tile: BM x BN outputs per workgroup, 2 x 2 wavefronts, each
+// wavefront FM x FN blocks of 32 x 32 accumulated with
+// v_mfma_f32_32x32x2_f32.
+template <int BM, int BN> struct Warps {
+  static constexpr int TM = BM / 2, TN = BN / 2;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static_assert(FM >= 1 && FN >= 1, "tile too small");
+};
+
+template <int BM, int BN, int BK>
+__device__ __forceinline__ void mma_tile(const f32x4* sA, const f32x4* sB,
+                                         f32x16 (&acc)[Warps<BM, BN>::FM][Warps<BM, BN>::FN]) {
+  using W = Warps<BM, BN>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, i = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int q = 0; q < BK / 8; ++q) {
+    f32x4 a[W::FM], b[W::FN];
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm)
+      a[fm] = sA[(2 * q + h) * TileShape<BM, BK>::PITCH + wm * W::TM + fm * 32 + i];
+#pragma unroll
+    for (int fn = 0; fn < W::FN; ++fn)
+      b[fn] = sB[(2 * q + h) * TileShape<BN, BK>::PITCH + wn * W::TN + fn * 32 + i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int fm = 0; fm < W::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < W::FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][c], b[fn][c],
+                                                             acc[fm][fn], 0, 0, 0);
+  }
+}
+
+// Row / column (within the BM x BN tile) of accumulator register v of
+// block (fm, fn) held by this lane (the 32x32 MFMA output layout: lane l
+// holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4).
+template <int BM, int BN>
+__device__ __forceinline__ int acc_row(int fm, int v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave >> 1) * Warps<BM, BN>::TM + fm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+template <int BM, int BN>
+__device__ __forceinline__ int acc_col(int fn) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave & 1) * Warps<BM, BN>::TN + fn * 32 + (lane & 31);
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.0f;
+}
+
+// Double-buffered main loop over the K tiles starting at kbase: the loaders
+// read tile kt into registers (global loads), store it to LDS, and
+// mma_tile consumes it.  One barrier per K tile: the next tile's stores go
+// to the other buffer, which every wavefront finished reading before the
+// previous barrier.
+template <int BM, int BN, int BK, class LA, class LB>
+__device__ __forceinline__ void gemm_mainloop(
+    LA& la, LB& lb, int kbase, int nk, f32x4* smem,
+    f32x16 (&acc)[Warps<BM, BN>::FM][Warps<BM, BN>::FN]) {
+  constexpr int CA = TileShape<BM, BK>::CELLS, CB = TileShape<BN, BK>::CELLS;
+  f32x4* sA[2] = {smem, smem + CA + CB};
+  f32x4* sB[2] = {smem + CA, smem + 2 * CA + CB};
+  if (nk <= 0) return;
+  la.load(kbase);
+  lb.load(kbase);
+  la.store(sA[0]);
+  lb.store(sB[0]);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.load(kbase + (kt + 1) * BK);
+      lb.load(kbase + (kt + 1) * BK);
+    }
+    mma_tile<BM, BN, BK>(sA[cur], sB[cur], acc);
+    if (more) {
+      la.store(sA[cur ^ 1]);
+      lb.store(sB[cur ^ 1]);
+    }
+    __syncthreads();
+  }
+}
+
+template <int BM, int BN, int BK>
+constexpr int mainloop_cells() {
+  return 2 * (TileShape<BM, BK>::CELLS + TileShape<BN, BK>::CELLS);
+}
+
+}  // namespace dion

@@ -1,0 +1,582 @@
+// libdion host side: argument validation, workspace layout, grouped launch
+// schedule and the C ABI declared in include/dion.h.
+//
+// One step (Orth-Dion page, equation block; Dion's rule from its closing
+// remark) is enqueued as:
+//   k_mv [+k_reduce]                 P = (G + R) V
+//   CholeskyQR2 on P -> U            2 x (k_gram, k_chol_*, k_trmm)
+//   k_mtu [+k_reduce]                W = (G + R)^T U
+//   Orth-Dion: CholeskyQR2 on W -> V     Dion: k_colnorm, k_colscale -> V
+//   k_epi                            X -= eta U V^T, R = beta (G + R - U W^T)
+// Every kernel is one grouped launch over all matrices of the call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <vector>
+
+#include "dion.h"
+#include "dion_types.h"
+#include "launchers.h"
+
+#define DION_API extern "C" __attribute__((visibility("default")))
+
+struct dion_plan;
+
+namespace dion {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTargetBlocks = 1024;   // split the reduction below this many tiles
+constexpr int kMinSplitLen = 256;     // shortest reduction slice worth a split
+constexpr int kBK = 32;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+// Output tile width: 128 unless that wastes more than 10% of the tile.
+int pick_bn(int cols) {
+  const int t128 = cdiv(cols, 128) * 128;
+  return cols * 10 >= t128 * 9 ? 128 : 64;
+}
+
+struct ClassRec {
+  int m, n, r, rp;
+  int first, count;
+  int bn_r, bn_n, bg;
+  int s_mv, kl_mv, s_mtu, kl_mtu, s_gp, kl_gp, s_gw, kl_gw;
+};
+
+}  // namespace
+}  // namespace dion
+
+struct dion_plan {
+  int count = 0, variant = 0, gdtype = 0;
+  bool vec = false;
+  bool single = false;
+  std::vector<dion::ClassRec> cls;
+  std::vector<dion::MatDesc> table;   // grouped order
+  size_t ws_bytes = 0, status_off = 0, table_off = 0;
+  dion::MatDesc* pinned = nullptr;    // pinned copy of `table` (grouped calls)
+  hipEvent_t ev = nullptr;
+  bool ev_pending = false;
+  std::vector<uint64_t> key;          // cache key (grouped calls)
+};
+
+namespace dion {
+namespace {
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int validate_matrix(const dion_matrix& a, int gdtype) {
+  if (!a.X || !a.G || !a.R || !a.V) return DION_ERR_INVALID_ARG;
+  if (a.m < 1 || a.n < 1 || a.m > DION_MAX_DIM || a.n > DION_MAX_DIM) return DION_ERR_INVALID_ARG;
+  if (a.m * a.n > INT32_MAX) return DION_ERR_INVALID_ARG;
+  if (a.r < 1 || a.r > std::min(a.m, a.n) || a.r > DION_MAX_RANK) return DION_ERR_INVALID_ARG;
+  const size_t eg = gdtype == DION_DTYPE_BF16 ? 2 : 4;
+  auto misaligned = [](const void* p, size_t al) { return reinterpret_cast<uintptr_t>(p) % al != 0; };
+  if (misaligned(a.X, 4) || misaligned(a.R, 4) || misaligned(a.V, 4) || misaligned(a.G, eg))
+    return DION_ERR_INVALID_ARG;
+  const size_t mn = static_cast<size_t>(a.m) * a.n, nr = static_cast<size_t>(a.n) * a.r;
+  const void* p[4] = {a.X, a.G, a.R, a.V};
+  const size_t s[4] = {mn * 4, mn * eg, mn * 4, nr * 4};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (ranges_overlap(p[i], s[i], p[j], s[j])) return DION_ERR_INVALID_ARG;
+  return DION_OK;
+}
+
+bool vec_ok(const dion_matrix& a, int gdtype) {
+  auto al = [](const void* p, size_t b) { return reinterpret_cast<uintptr_t>(p) % b == 0; };
+  return a.n % 4 == 0 && a.r % 4 == 0 && al(a.X, 16) && al(a.R, 16) && al(a.V, 16) &&
+         al(a.G, gdtype == DION_DTYPE_BF16 ? 8 : 16);
+}
+
+// Split count and slice length for a reduction of length K when the launch
+// has `tiles` output tiles in total.
+void pick_split(int64_t tiles, int K, int& s, int& klen) {
+  s = 1;
+  if (tiles < kTargetBlocks / 2) {
+    s = cdiv(kTargetBlocks, tiles);
+    s = std::max(1, std::min(s, K / kMinSplitLen));
+  }
+  klen = cdiv(cdiv(K, s), kBK) * kBK;
+  s = cdiv(K, klen);
+}
+
+// Builds classes, split choices and the workspace layout.  Host only.
+int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool single,
+               dion_plan& p) {
+  if (!mats || count < 1) return DION_ERR_INVALID_ARG;
+  if (variant != DION_VARIANT_DION && variant != DION_VARIANT_ORTH) return DION_ERR_INVALID_ARG;
+  if (gdtype != DION_DTYPE_F32 && gdtype != DION_DTYPE_BF16) return DION_ERR_INVALID_ARG;
+  p.count = count;
+  p.variant = variant;
+  p.gdtype = gdtype;
+  p.single = single;
+  p.vec = true;
+  for (int i = 0; i < count; ++i) {
+    const int rc = validate_matrix(mats[i], gdtype);
+    if (rc != DION_OK) return rc;
+    p.vec = p.vec && vec_ok(mats[i], gdtype);
+  }
+  // Classes by shape, in order of first appearance.
+  std::vector<int> cls_of(count, -1);
+  for (int i = 0; i < count; ++i) {
+    int c = 0;
+    for (; c < static_cast<int>(p.cls.size()); ++c)
+      if (p.cls[c].m == mats[i].m && p.cls[c].n == mats[i].n && p.cls[c].r == mats[i].r) break;
+    if (c == static_cast<int>(p.cls.size())) {
+      ClassRec k{};
+      k.m = static_cast<int>(mats[i].m);
+      k.n = static_cast<int>(mats[i].n);
+      k.r = static_cast<int>(mats[i].r);
+      k.rp = cdiv(k.r, kCholNB) * kCholNB;
+      k.bn_r = pick_bn(k.r);
+      k.bn_n = pick_bn(k.n);
+      k.bg = pick_bn(k.r);
+      p.cls.push_back(k);
+    }
+    cls_of[i] = c;
+    p.cls[c].count++;
+  }
+  int first = 0;
+  for (auto& k : p.cls) {
+    k.first = first;
+    first += k.count;
+  }
+  // Reduction splits, from the total tile count of each grouped launch.
+  int64_t t_mv = 0, t_mtu = 0, t_gp = 0, t_gw = 0;
+  for (auto& k : p.cls) {
+    const int nt = cdiv(k.r, k.bg);
+    t_mv += static_cast<int64_t>(k.count) * cdiv(k.m, 128) * cdiv(k.r, k.bn_r);
+    t_mtu += static_cast<int64_t>(k.count) * cdiv(k.n, 128) * cdiv(k.r, k.bn_r);
+    t_gp += static_cast<int64_t>(k.count) * nt * (nt + 1) / 2;
+  }
+  t_gw = t_gp;
+  for (auto& k : p.cls) {
+    pick_split(t_mv, k.n, k.s_mv, k.kl_mv);
+    pick_split(t_mtu, k.m, k.s_mtu, k.kl_mtu);
+    pick_split(t_gp, k.m, k.s_gp, k.kl_gp);
+    pick_split(t_gw, k.n, k.s_gw, k.kl_gw);
+  }
+  // Workspace: status words | matrix table (grouped calls) | per-matrix buffers.
+  size_t off = 0;
+  p.status_off = off;
+  off = align_up(off + static_cast<size_t>(count) * 4);
+  p.table_off = off;
+  if (!single) off = align_up(off + static_cast<size_t>(count) * sizeof(MatDesc));
+  p.table.resize(count);
+  std::vector<int> next(p.cls.size());
+  for (size_t c = 0; c < p.cls.size(); ++c) next[c] = p.cls[c].first;
+  std::vector<int> pos(count);
+  for (int i = 0; i < count; ++i) pos[i] = next[cls_of[i]]++;
+  std::vector<int> order(count);
+  for (int i = 0; i < count; ++i) order[pos[i]] = i;
+  for (int g = 0; g < count; ++g) {
+    const int i = order[g];
+    const ClassRec& k = p.cls[cls_of[i]];
+    const dion_matrix& a = mats[i];
+    MatDesc d{};
+    d.X = a.X;
+    d.G = a.G;
+    d.R = a.R;
+    d.V = a.V;
+    d.m = k.m;
+    d.n = k.n;
+    d.r = k.r;
+    d.rp = k.rp;
+    d.slot = i;
+    const size_t m = k.m, n = k.n, r = k.r, rp = k.rp;
+    auto take = [&](size_t bytes) {
+      const size_t o = off;
+      off = align_up(off + bytes);
+      return static_cast<int64_t>(o);
+    };
+    d.oP = take(m * r * 4);
+    d.oB = take(std::max(m, n) * r * 4);
+    d.oW = take(n * r * 4);
+    d.oS = take(static_cast<size_t>(std::max(k.s_gp, k.s_gw)) * rp * rp * 4);
+    d.oA = take(rp * rp * 8);
+    d.oY = take(rp * rp * 8);
+    d.oD = take((kCholNB * kCholNB + rp) * 8);
+    d.oN = take(r * 4);
+    const size_t kpart = std::max(k.s_mv > 1 ? k.s_mv * m * r : 0, k.s_mtu > 1 ? k.s_mtu * n * r : 0);
+    d.oK = kpart ? take(kpart * 4) : 0;
+    p.table[g] = d;
+  }
+  p.ws_bytes = off;
+  return DION_OK;
+}
+
+// One grouped launch per batch of at most kMaxClasses classes.  `fill`
+// sets the per-class work shape (returns false to leave a class out).
+template <class Fill, class Go>
+hipError_t grouped(const dion_plan& p, const Launch& base, Fill fill, Go go) {
+  Launch L = base;
+  L.nclass = 0;
+  L.total = 0;
+  for (const ClassRec& c : p.cls) {
+    ClassInfo ci{};
+    if (!fill(c, ci) || ci.tiles <= 0) continue;
+    ci.first = c.first;
+    ci.count = c.count;
+    ci.base = L.total;
+    L.cls[L.nclass++] = ci;
+    L.total += c.count * ci.tiles;
+    if (L.nclass == kMaxClasses) {
+      const hipError_t e = go(L);
+      if (e != hipSuccess) return e;
+      L.nclass = 0;
+      L.total = 0;
+    }
+  }
+  if (L.nclass > 0) return go(L);
+  return hipSuccess;
+}
+
+#define DION_TRY(expr)                         \
+  do {                                         \
+    const hipError_t e_ = (expr);              \
+    if (e_ != hipSuccess) return e_;           \
+  } while (0)
+
+// CholeskyQR2 of the P (which = 0) or W (which = 1) factor.
+hipError_t orth(const dion_plan& p, Launch base, int which, hipStream_t st) {
+  base.which = which;
+  base.flag = which == 0 ? DION_STATUS_ORTH_P : DION_STATUS_ORTH_W;
+  int max_nblk = 0;
+  for (const ClassRec& c : p.cls) max_nblk = std::max(max_nblk, c.rp / kCholNB);
+  for (int pass = 1; pass <= 2; ++pass) {
+    base.pass = pass;
+    for (int bg : {128, 64}) {
+      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+        if (c.bg != bg) return false;
+        const int nt = cdiv(c.r, bg);
+        ci.tx = nt;
+        ci.splits = which == 0 ? c.s_gp : c.s_gw;
+        ci.klen = which == 0 ? c.kl_gp : c.kl_gw;
+        ci.tiles = nt * (nt + 1) / 2 * ci.splits;
+        return true;
+      }, [&](const Launch& L) { return launch_gram(L, bg, p.vec, st); }));
+    }
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      const int nb = c.rp / kCholNB;
+      ci.splits = which == 0 ? c.s_gp : c.s_gw;
+      ci.tiles = nb * (nb + 1) / 2;
+      return true;
+    }, [&](const Launch& L) { return launch_chol_init(L, st); }));
+    for (int kb = 0; kb < max_nblk; ++kb) {
+      base.kb = kb;
+      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+        ci.tiles = c.rp / kCholNB > kb ? 1 : 0;
+        return true;
+      }, [&](const Launch& L) { return launch_chol_diag(L, st); }));
+      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+        const int nb = c.rp / kCholNB;
+        ci.tiles = nb > kb ? nb - 1 : 0;
+        return true;
+      }, [&](const Launch& L) { return launch_chol_panel(L, st); }));
+      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+        const int nl = c.rp / kCholNB - kb - 1;
+        ci.tiles = nl > 0 ? nl * (nl + 1) / 2 + nl * (kb + 1) : 0;
+        return true;
+      }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
+    }
+    for (int bn : {128, 64}) {
+      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+        if (c.bn_r != bn) return false;
+        ci.tx = cdiv(which == 0 ? c.m : c.n, 128);
+        ci.ty = cdiv(c.r, bn);
+        ci.tiles = ci.tx * ci.ty;
+        return true;
+      }, [&](const Launch& L) { return launch_trmm(L, bn, p.vec, st); }));
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, float beta,
+                    char* ws, hipStream_t st) {
+  Launch base{};
+  base.table = dev_table;
+  if (p.single) base.inl = p.table[0];
+  base.ws = ws;
+  base.status = reinterpret_cast<int32_t*>(ws + p.status_off);
+  base.eta = eta;
+  base.beta = beta;
+  const int ept = elems_per_tile();
+
+  // P = M V
+  for (int bn : {128, 64}) {
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      if (c.bn_r != bn) return false;
+      ci.tx = cdiv(c.m, 128);
+      ci.ty = cdiv(c.r, bn);
+      ci.splits = c.s_mv;
+      ci.klen = c.kl_mv;
+      ci.tiles = ci.tx * ci.ty * ci.splits;
+      return true;
+    }, [&](const Launch& L) { return launch_mv(L, p.gdtype, bn, p.vec, st); }));
+  }
+  base.which = 0;
+  DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+    if (c.s_mv <= 1) return false;
+    ci.splits = c.s_mv;
+    ci.tiles = cdiv(static_cast<int64_t>(c.m) * c.r, ept);
+    return true;
+  }, [&](const Launch& L) { return launch_reduce(L, st); }));
+
+  // U = orth(P)
+  DION_TRY(orth(p, base, 0, st));
+
+  // W = M^T U
+  for (int bn : {128, 64}) {
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      if (c.bn_r != bn) return false;
+      ci.tx = cdiv(c.n, 128);
+      ci.ty = cdiv(c.r, bn);
+      ci.splits = c.s_mtu;
+      ci.klen = c.kl_mtu;
+      ci.tiles = ci.tx * ci.ty * ci.splits;
+      return true;
+    }, [&](const Launch& L) { return launch_mtu(L, p.gdtype, bn, p.vec, st); }));
+  }
+  base.which = 1;
+  DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+    if (c.s_mtu <= 1) return false;
+    ci.splits = c.s_mtu;
+    ci.tiles = cdiv(static_cast<int64_t>(c.n) * c.r, ept);
+    return true;
+  }, [&](const Launch& L) { return launch_reduce(L, st); }));
+
+  // Vbar into V
+  if (p.variant == DION_VARIANT_ORTH) {
+    DION_TRY(orth(p, base, 1, st));
+  } else {
+    base.flag = DION_STATUS_COLNORM;
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      ci.tiles = cdiv(c.r, 64);
+      return true;
+    }, [&](const Launch& L) { return launch_colnorm(L, st); }));
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      ci.tiles = cdiv(static_cast<int64_t>(c.n) * c.r, ept);
+      return true;
+    }, [&](const Launch& L) { return launch_colscale(L, st); }));
+  }
+
+  // X and R
+  for (int bn : {128, 64}) {
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      if (c.bn_n != bn) return false;
+      ci.tx = cdiv(c.m, 128);
+      ci.ty = cdiv(c.n, bn);
+      ci.tiles = ci.tx * ci.ty;
+      return true;
+    }, [&](const Launch& L) { return launch_epi(L, p.gdtype, bn, p.vec, st); }));
+  }
+  return hipSuccess;
+}
+
+int check_call(const dion_plan& p, float eta, float beta, const void* ws, size_t bytes) {
+  if (!std::isfinite(eta) || !std::isfinite(beta)) return DION_ERR_INVALID_ARG;
+  if (!ws || bytes < p.ws_bytes) return DION_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return DION_ERR_WORKSPACE;
+  return DION_OK;
+}
+
+void plan_free(dion_plan* p) {
+  if (!p) return;
+  if (p->ev) {
+    if (p->ev_pending) (void)hipEventSynchronize(p->ev);
+    (void)hipEventDestroy(p->ev);
+  }
+  if (p->pinned) (void)hipHostFree(p->pinned);
+  delete p;
+}
+
+int plan_alloc_host(dion_plan* p) {
+  if (hipHostMalloc(reinterpret_cast<void**>(&p->pinned), sizeof(MatDesc) * p->count,
+                    hipHostMallocDefault) != hipSuccess) {
+    p->pinned = nullptr;
+    return DION_ERR_HIP;
+  }
+  std::memcpy(p->pinned, p->table.data(), sizeof(MatDesc) * p->count);
+  if (hipEventCreateWithFlags(&p->ev, hipEventDisableTiming) != hipSuccess) {
+    p->ev = nullptr;
+    return DION_ERR_HIP;
+  }
+  return DION_OK;
+}
+
+int plan_step(dion_plan* p, float eta, float beta, void* ws, size_t bytes, hipStream_t st) {
+  int rc = check_call(*p, eta, beta, ws, bytes);
+  if (rc != DION_OK) return rc;
+  char* w = static_cast<char*>(ws);
+  MatDesc* dev_table = reinterpret_cast<MatDesc*>(w + p->table_off);
+  if (hipMemcpyAsync(dev_table, p->pinned, sizeof(MatDesc) * p->count, hipMemcpyHostToDevice,
+                     st) != hipSuccess)
+    return DION_ERR_HIP;
+  if (hipEventRecord(p->ev, st) != hipSuccess) return DION_ERR_HIP;
+  p->ev_pending = true;
+  return run_step(*p, dev_table, eta, beta, w, st) == hipSuccess ? DION_OK : DION_ERR_HIP;
+}
+
+// Cache of grouped plans keyed by the matrix list (most recent first).
+constexpr size_t kCacheSize = 8;
+std::mutex g_cache_mu;
+std::list<dion_plan*> g_cache;
+
+std::vector<uint64_t> make_key(const dion_matrix* mats, int count, int variant, int gdtype) {
+  std::vector<uint64_t> k;
+  k.reserve(3 + 7 * static_cast<size_t>(count));
+  k.push_back(static_cast<uint64_t>(count));
+  k.push_back(static_cast<uint64_t>(variant));
+  k.push_back(static_cast<uint64_t>(gdtype));
+  for (int i = 0; i < count; ++i) {
+    k.push_back(reinterpret_cast<uintptr_t>(mats[i].X));
+    k.push_back(reinterpret_cast<uintptr_t>(mats[i].G));
+    k.push_back(reinterpret_cast<uintptr_t>(mats[i].R));
+    k.push_back(reinterpret_cast<uintptr_t>(mats[i].V));
+    k.push_back(static_cast<uint64_t>(mats[i].m));
+    k.push_back(static_cast<uint64_t>(mats[i].n));
+    k.push_back(static_cast<uint64_t>(mats[i].r));
+  }
+  return k;
+}
+
+}  // namespace
+}  // namespace dion
+
+using namespace dion;
+
+DION_API int dion_version(void) { return 100; }
+
+DION_API const char* dion_error_string(int code) {
+  switch (code) {
+    case DION_OK: return "success";
+    case DION_ERR_INVALID_ARG: return "invalid argument";
+    case DION_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case DION_ERR_HIP: return "HIP runtime error";
+    case DION_ERR_BREAKDOWN: return "numerical breakdown (rank-deficient or non-finite factor)";
+    default: return "unknown error code";
+  }
+}
+
+DION_API size_t dion_workspace_size(int64_t m, int64_t n, int64_t r, int variant, int g_dtype) {
+  // Shape-only query: dummy, distinct, aligned addresses stand in for the
+  // buffers so validation sees a well-formed call.
+  dion_matrix a{};
+  a.X = reinterpret_cast<float*>(uintptr_t{1} << 40);
+  a.G = reinterpret_cast<const void*>(uintptr_t{2} << 40);
+  a.R = reinterpret_cast<float*>(uintptr_t{3} << 40);
+  a.V = reinterpret_cast<float*>(uintptr_t{4} << 40);
+  a.m = m;
+  a.n = n;
+  a.r = r;
+  dion_plan p;
+  if (build_plan(&a, 1, variant, g_dtype, true, p) != DION_OK) return 0;
+  return p.ws_bytes;
+}
+
+DION_API int dion_step(float* X, const void* G, float* R, float* V, int64_t m, int64_t n,
+                       int64_t r, float eta, float beta, int variant, int g_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  dion_matrix a{X, G, R, V, m, n, r};
+  dion_plan p;
+  int rc = build_plan(&a, 1, variant, g_dtype, true, p);
+  if (rc != DION_OK) return rc;
+  rc = check_call(p, eta, beta, workspace, workspace_bytes);
+  if (rc != DION_OK) return rc;
+  const hipError_t e = run_step(p, nullptr, eta, beta, static_cast<char*>(workspace),
+                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DION_OK : DION_ERR_HIP;
+}
+
+DION_API size_t dion_workspace_size_batched(const dion_matrix* mats, int count, int variant,
+                                            int g_dtype) {
+  dion_plan p;
+  if (build_plan(mats, count, variant, g_dtype, false, p) != DION_OK) return 0;
+  return p.ws_bytes;
+}
+
+DION_API int dion_plan_create(const dion_matrix* mats, int count, int variant, int g_dtype,
+                              dion_plan** plan_out) {
+  if (!plan_out) return DION_ERR_INVALID_ARG;
+  *plan_out = nullptr;
+  dion_plan* p = new (std::nothrow) dion_plan();
+  if (!p) return DION_ERR_INVALID_ARG;
+  int rc = build_plan(mats, count, variant, g_dtype, false, *p);
+  if (rc == DION_OK) rc = plan_alloc_host(p);
+  if (rc != DION_OK) {
+    plan_free(p);
+    return rc;
+  }
+  *plan_out = p;
+  return DION_OK;
+}
+
+DION_API size_t dion_plan_workspace_size(const dion_plan* plan) {
+  return plan ? plan->ws_bytes : 0;
+}
+
+DION_API int dion_plan_count(const dion_plan* plan) { return plan ? plan->count : 0; }
+
+DION_API int dion_plan_step(dion_plan* plan, float eta, float beta, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!plan) return DION_ERR_INVALID_ARG;
+  return plan_step(plan, eta, beta, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+DION_API void dion_plan_destroy(dion_plan* plan) { plan_free(plan); }
+
+DION_API int dion_step_batched(const dion_matrix* mats, int count, float eta, float beta,
+                               int variant, int g_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!mats || count < 1) return DION_ERR_INVALID_ARG;
+  std::vector<uint64_t> key = make_key(mats, count, variant, g_dtype);
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  dion_plan* hit = nullptr;
+  for (auto it = g_cache.begin(); it != g_cache.end(); ++it)
+    if ((*it)->key == key) {
+      hit = *it;
+      g_cache.erase(it);
+      break;
+    }
+  if (!hit) {
+    dion_plan* p = nullptr;
+    const int rc = dion_plan_create(mats, count, variant, g_dtype, &p);
+    if (rc != DION_OK) return rc;
+    p->key = std::move(key);
+    hit = p;
+    if (g_cache.size() >= kCacheSize) {
+      plan_free(g_cache.back());
+      g_cache.pop_back();
+    }
+  }
+  g_cache.push_front(hit);
+  return plan_step(hit, eta, beta, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+DION_API int dion_status(const void* workspace, int count, void* stream, int* per_matrix) {
+  if (!workspace || count < 1) return DION_ERR_INVALID_ARG;
+  std::vector<int32_t> st(count);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(st.data(), workspace, sizeof(int32_t) * count, hipMemcpyDeviceToHost, s) !=
+      hipSuccess)
+    return DION_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return DION_ERR_HIP;
+  int rc = DION_OK;
+  for (int i = 0; i < count; ++i) {
+    if (per_matrix) per_matrix[i] = st[i];
+    if (st[i] != 0) rc = DION_ERR_BREAKDOWN;
+  }
+  return rc;
+}

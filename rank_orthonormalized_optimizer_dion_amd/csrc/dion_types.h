@@ -1,0 +1,61 @@
+// Types shared by the host scheduler and the gfx950 kernels of libdion.
+#pragma once
+#include <stdint.h>
+
+namespace dion {
+
+// Block size of the float64 Cholesky / triangular-inverse kernels.
+constexpr int kCholNB = 64;
+// Grouped launches carry at most this many shape classes.
+constexpr int kMaxClasses = 8;
+
+// One matrix as the kernels see it.  Workspace offsets are bytes from the
+// workspace base.  rp = r rounded up to kCholNB.
+struct MatDesc {
+  float* X;
+  const void* G;
+  float* R;
+  float* V;
+  int32_t m, n, r, rp;
+  int32_t slot;      // index in the caller's list = status word index
+  int32_t pad0;
+  int64_t oP;        // m x r      float32: P = M V, then U
+  int64_t oB;        // max(m,n) x r float32: first CholeskyQR pass output
+  int64_t oW;        // n x r      float32: W = M^T U
+  int64_t oS;        // splits x rp x rp float32: Gram partial sums
+  int64_t oA;        // rp x rp    float64: Cholesky work matrix (upper blocks)
+  int64_t oY;        // rp x rp    float64: T^{-T} (lower blocks)
+  int64_t oD;        // kCholNB^2 + rp float64: diagonal-block inverse, diag(S)
+  int64_t oN;        // r          float32: inverse column norms (Dion)
+  int64_t oK;        // split-K partial products (float32)
+};
+
+// Matrices with the same (m, n, r) form a class; inside one launch every
+// matrix of a class owns `tiles` consecutive work items starting at `base`.
+struct ClassInfo {
+  int32_t first;   // first matrix (index into the grouped table)
+  int32_t count;   // matrices in the class
+  int32_t tiles;   // work items per matrix in this launch
+  int32_t base;    // first work item of the class in this launch
+  int32_t tx, ty;  // tile grid of one matrix (x: rows, y: cols)
+  int32_t splits;  // split of the reduction dimension
+  int32_t klen;    // reduction length per split (multiple of the K tile)
+};
+
+// Kernel argument block of one grouped launch (passed by value).
+struct Launch {
+  const MatDesc* table;   // device table, or nullptr to use `inl`
+  MatDesc inl;            // the single matrix of a dion_step call
+  char* ws;               // workspace base
+  int32_t* status;        // status words (one per matrix slot)
+  int32_t nclass;
+  int32_t total;          // work items in the launch
+  ClassInfo cls[kMaxClasses];
+  float eta, beta;
+  int32_t kb;             // Cholesky block step
+  int32_t which;          // 0: factor P (m rows), 1: factor W (n rows)
+  int32_t pass;           // CholeskyQR pass 1 or 2
+  int32_t flag;           // status bit of this factorization
+};
+
+}  // namespace dion

@@ -1,0 +1,248 @@
+// float64 Cholesky factorization S = T^T T (T upper triangular, positive
+// diagonal) of the Gram matrix of a CholeskyQR pass, together with
+// Y = T^{-T}, in blocks of 64 (kCholNB).  orth(Q) = Q T^{-1} is then one
+// float32 MFMA product (k_trmm).  Y comes out of the same sweep: the row
+// operations of the right-looking factorization are applied to an identity
+// block column, i.e. forward substitution of T^T Y = I.
+//
+// Per block step kb (host loop):
+//   k_chol_diag   factor the diagonal block, Dinv = T_kk^{-1}, Y_kk = T_kk^{-T}
+//   k_chol_panel  T_kj = T_kk^{-T} A_kj (j > kb);  Y_kc = T_kk^{-T} Y_kc (c < kb)
+//   k_chol_trail  A_ij -= T_ki^T T_kj (kb < i <= j);  Y_ic -= T_ki^T Y_kc (c <= kb)
+// k_chol_init sums the Gram partials into A (float64) first and pads the
+// rows past r with the identity.
+#include <math.h>
+
+#include "device_common.h"
+#include "launchers.h"
+
+namespace dion {
+
+namespace {
+
+constexpr int NB = kCholNB;
+constexpr int LP = NB + 1;   // LDS row pitch (doubles)
+
+// A pivot below this fraction of the column's original squared norm means
+// the column is numerically dependent on the previous ones at float32
+// resolution (condition number beyond ~1e3): the factor is declared
+// rank-deficient.
+constexpr double kPivotTol = 1e-6;
+
+__device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
+  return L.status[d.slot] != 0;
+}
+
+__device__ __forceinline__ double* dptr(const Launch& L, int64_t off) {
+  return reinterpret_cast<double*>(L.ws + off);
+}
+
+// Load a 64 x 64 block at src (row pitch ld doubles) into LDS.
+__device__ __forceinline__ void load_block(double (*dst)[LP], const double* src, int64_t ld) {
+  for (int e = threadIdx.x; e < NB * NB / 2; e += kThreads) {
+    const int i = e / (NB / 2), j2 = e % (NB / 2);
+    const double2 v = *reinterpret_cast<const double2*>(src + i * ld + 2 * j2);
+    dst[i][2 * j2] = v.x;
+    dst[i][2 * j2 + 1] = v.y;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int nblk = d.rp / NB;
+  int p = local, bi = 0;
+  while (p >= nblk - bi) {
+    p -= nblk - bi;
+    ++bi;
+  }
+  const int bj = bi + p;
+  const float* S = reinterpret_cast<const float*>(L.ws + d.oS);
+  double* A = dptr(L, d.oA);
+  double* Sd = dptr(L, d.oD) + NB * NB;
+  const int64_t rp = d.rp, plane = rp * rp;
+  for (int e = threadIdx.x; e < NB * NB; e += kThreads) {
+    const int gi = bi * NB + e / NB, gj = bj * NB + e % NB;
+    double v;
+    if (gi < d.r && gj < d.r) {
+      v = 0.0;
+      for (int s = 0; s < ci.splits; ++s) v += static_cast<double>(S[s * plane + gi * rp + gj]);
+    } else {
+      v = gi == gj ? 1.0 : 0.0;
+    }
+    A[gi * rp + gj] = v;
+    if (gi == gj) Sd[gi] = v;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
+  __shared__ double a[NB][LP];
+  __shared__ double z[NB][LP];
+  __shared__ int bad;
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int kb = L.kb;
+  const int64_t rp = d.rp, o = static_cast<int64_t>(kb) * NB;
+  double* A = dptr(L, d.oA);
+  double* Y = dptr(L, d.oY);
+  double* Dinv = dptr(L, d.oD);
+  const double* Sd = Dinv + NB * NB + o;
+  load_block(a, A + o * rp + o, rp);
+  for (int e = threadIdx.x; e < NB * NB; e += kThreads) z[e / NB][e % NB] = (e / NB == e % NB) ? 1.0 : 0.0;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  const int tid = threadIdx.x;
+  for (int k = 0; k < NB; ++k) {
+    if (tid < NB) {   // wavefront 0: pivot and row k of T and of Y
+      const double dk = a[k][k];
+      const bool ok = dk > kPivotTol * Sd[k] && dk < INFINITY;
+      const double t = sqrt(dk), inv = 1.0 / t;
+      if (!ok && tid == 0) bad = 1;
+      if (tid > k) a[k][tid] *= inv;
+      else if (tid == k) a[k][k] = t;
+      if (tid <= k) z[k][tid] *= inv;
+    }
+    __syncthreads();
+    if (bad) break;
+    for (int e = tid; e < NB * NB; e += kThreads) {
+      const int i = e / NB, j = e % NB;
+      if (i <= k) continue;
+      if (j >= i) a[i][j] -= a[k][i] * a[k][j];
+      else if (j <= k) z[i][j] -= a[k][i] * z[k][j];
+    }
+    __syncthreads();
+  }
+  if (bad) {
+    if (tid == 0) atomicOr(&L.status[d.slot], L.flag);
+    return;
+  }
+  // Dinv = T_kk^{-1} = z^T (upper), Y_kk = z (lower, zeros above).
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int i = e / NB, j = e % NB;
+    Dinv[e] = i <= j ? z[j][i] : 0.0;
+    Y[(o + i) * rp + o + j] = z[i][j];
+  }
+}
+
+// out = Dinv^T * in for one 64 x 64 block, in place.
+__global__ __launch_bounds__(kThreads) void k_chol_panel(Launch L) {
+  __shared__ double dl[NB][LP];
+  __shared__ double in[NB][LP];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int kb = L.kb, nblk = d.rp / NB;
+  const int64_t rp = d.rp, o = static_cast<int64_t>(kb) * NB;
+  const int right = nblk - kb - 1;
+  double* blk = local < right ? dptr(L, d.oA) + o * rp + (kb + 1 + local) * NB
+                              : dptr(L, d.oY) + o * rp + (local - right) * NB;
+  load_block(dl, dptr(L, d.oD), NB);
+  load_block(in, blk, rp);
+  __syncthreads();
+  const int ta = threadIdx.x / 16, tb = threadIdx.x % 16;
+  double acc[4][4] = {};
+  const int emax = 4 * ta + 3;   // Dinv[e][a] = 0 for e > a
+  for (int e = 0; e <= emax; ++e) {
+    double x[4], y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[u] = dl[e][4 * ta + u];
+      y[u] = in[e][4 * tb + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc[u][w] += x[u] * y[w];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) blk[(4 * ta + u) * rp + 4 * tb + w] = acc[u][w];
+}
+
+// Trailing update of the factorization and of the identity block columns.
+__global__ __launch_bounds__(kThreads) void k_chol_trail(Launch L) {
+  __shared__ double lt[NB][LP];
+  __shared__ double rt[NB][LP];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int kb = L.kb, nblk = d.rp / NB;
+  const int64_t rp = d.rp, o = static_cast<int64_t>(kb) * NB;
+  const int nl = nblk - kb - 1;
+  const int nsym = nl * (nl + 1) / 2;
+  double* A = dptr(L, d.oA);
+  double* Y = dptr(L, d.oY);
+  const double* left;
+  const double* rgt;
+  double* out;
+  bool assign = false;
+  if (local < nsym) {
+    int p = local, i = 0;
+    while (p >= nl - i) {
+      p -= nl - i;
+      ++i;
+    }
+    const int bi = kb + 1 + i, bj = bi + p;
+    left = A + o * rp + bi * NB;
+    rgt = A + o * rp + bj * NB;
+    out = A + static_cast<int64_t>(bi) * NB * rp + bj * NB;
+  } else {
+    const int t = local - nsym;
+    const int bi = kb + 1 + t / (kb + 1), c = t % (kb + 1);
+    left = A + o * rp + bi * NB;
+    rgt = Y + o * rp + c * NB;
+    out = Y + static_cast<int64_t>(bi) * NB * rp + c * NB;
+    assign = c == kb;   // first write of this block of Y
+  }
+  load_block(lt, left, rp);
+  load_block(rt, rgt, rp);
+  __syncthreads();
+  const int ta = threadIdx.x / 16, tb = threadIdx.x % 16;
+  double acc[4][4] = {};
+  for (int e = 0; e < NB; ++e) {
+    double x[4], y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[u] = lt[e][4 * ta + u];
+      y[u] = rt[e][4 * tb + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc[u][w] += x[u] * y[w];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      double* q = out + (4 * ta + u) * rp + 4 * tb + w;
+      *q = assign ? -acc[u][w] : *q - acc[u][w];
+    }
+}
+
+template <class K>
+hipError_t go(K kernel, const Launch& L, hipStream_t st) {
+  if (L.total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(L.total), dim3(kThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chol_init(const Launch& L, hipStream_t st) { return go(k_chol_init, L, st); }
+hipError_t launch_chol_diag(const Launch& L, hipStream_t st) { return go(k_chol_diag, L, st); }
+hipError_t launch_chol_panel(const Launch& L, hipStream_t st) { return go(k_chol_panel, L, st); }
+hipError_t launch_chol_trail(const Launch& L, hipStream_t st) { return go(k_chol_trail, L, st); }
+
+}  // namespace dion

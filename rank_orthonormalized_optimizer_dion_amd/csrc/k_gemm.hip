@@ -1,0 +1,280 @@
+// The dense contractions of one Dion / Orth-Dion step, as grouped float32
+// MFMA kernels for gfx950 (Orth-Dion page, equation block):
+//   k_mv    P = M V            (M = G + R formed while loading)
+//   k_mtu   W = M^T U          (equation 3)
+//   k_gram  S = Q^T Q          (Gram matrix of a CholeskyQR pass)
+//   k_trmm  Q' = Q T^{-1}      (T^{-1} upper triangular, read from T^{-T})
+//   k_epi   X -= eta U Vbar^T and R = beta (M - U W^T)   (equations 5, 6)
+#include "device_common.h"
+#include "launchers.h"
+
+namespace dion {
+
+namespace {
+
+constexpr int BM = 128;
+
+template <int TBM, int TBN>
+__device__ __forceinline__ void store_tile(float* out, int64_t ld, int r0, int c0,
+                                           int rmax, int cmax,
+                                           const f32x16 (&acc)[Warps<TBM, TBN>::FM][Warps<TBM, TBN>::FN]) {
+  using W = Warps<TBM, TBN>;
+#pragma unroll
+  for (int fm = 0; fm < W::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < W::FN; ++fn) {
+      const int col = c0 + acc_col<TBM, TBN>(fn);
+      if (col >= cmax) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = r0 + acc_row<TBM, TBN>(fm, v);
+        if (row < rmax) out[static_cast<int64_t>(row) * ld + col] = acc[fm][fn][v];
+      }
+    }
+}
+
+__device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
+  return L.status[d.slot] != 0;
+}
+
+// P = (G + R) V over the reduction slice [kbeg, kend) of n.
+template <typename GT, int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_mv(Launch L) {
+  constexpr int BK = 32;
+  __shared__ f32x4 smem[mainloop_cells<BM, BN, BK>()];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  // The first kernel of a step clears the matrix's status word.
+  if (local == 0 && threadIdx.x == 0) L.status[d.slot] = 0;
+  const int per = ci.tx * ci.ty;
+  const int s = local / per, rem = local - s * per;
+  const int tm = rem / ci.ty, tn = rem - tm * ci.ty;
+  const int kbeg = s * ci.klen;
+  const int kend = min(d.n, kbeg + ci.klen);
+  LoadKC<BM, BK, VEC, false, SrcM<GT>> la(
+      SrcM<GT>{static_cast<const GT*>(d.G), d.R}, d.n, tm * BM, d.m, kend);
+  LoadXC<BN, BK, VEC, SrcF32> lb(SrcF32{d.V}, d.r, tn * BN, d.r, kend);
+  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
+  zero_acc(acc);
+  gemm_mainloop<BM, BN, BK>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
+  float* out = ci.splits == 1
+                   ? reinterpret_cast<float*>(L.ws + d.oP)
+                   : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.m * d.r;
+  store_tile<BM, BN>(out, d.r, tm * BM, tn * BN, d.m, d.r, acc);
+}
+
+// W = (G + R)^T U over the reduction slice [kbeg, kend) of m.
+template <typename GT, int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_mtu(Launch L) {
+  constexpr int BK = 32;
+  __shared__ f32x4 smem[mainloop_cells<BM, BN, BK>()];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int per = ci.tx * ci.ty;
+  const int s = local / per, rem = local - s * per;
+  const int tm = rem / ci.ty, tn = rem - tm * ci.ty;
+  const int kbeg = s * ci.klen;
+  const int kend = min(d.m, kbeg + ci.klen);
+  LoadXC<BM, BK, VEC, SrcM<GT>> la(
+      SrcM<GT>{static_cast<const GT*>(d.G), d.R}, d.n, tm * BM, d.n, kend);
+  const float* U = reinterpret_cast<const float*>(L.ws + d.oP);
+  LoadXC<BN, BK, VEC, SrcF32> lb(SrcF32{U}, d.r, tn * BN, d.r, kend);
+  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
+  zero_acc(acc);
+  gemm_mainloop<BM, BN, BK>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
+  float* out = ci.splits == 1
+                   ? reinterpret_cast<float*>(L.ws + d.oW)
+                   : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.n * d.r;
+  store_tile<BM, BN>(out, d.r, tm * BM, tn * BN, d.n, d.r, acc);
+}
+
+__device__ __forceinline__ const float* qr_source(const Launch& L, const MatDesc& d) {
+  const int64_t off = L.pass == 1 ? (L.which == 0 ? d.oP : d.oW) : d.oB;
+  return reinterpret_cast<const float*>(L.ws + off);
+}
+
+// Partial Gram matrix S_s = Q[kbeg:kend]^T Q[kbeg:kend] on the upper
+// triangle of BG x BG tiles.
+template <int BG, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_gram(Launch L) {
+  constexpr int BK = 32;
+  __shared__ f32x4 smem[mainloop_cells<BG, BG, BK>()];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int rows = L.which == 0 ? d.m : d.n;
+  const int nt = ci.tx;
+  const int pairs = nt * (nt + 1) / 2;
+  const int s = local / pairs;
+  int p = local - s * pairs;
+  int ti = 0;
+  while (p >= nt - ti) {
+    p -= nt - ti;
+    ++ti;
+  }
+  const int tj = ti + p;
+  const int kbeg = s * ci.klen;
+  const int kend = min(rows, kbeg + ci.klen);
+  const float* Q = qr_source(L, d);
+  LoadXC<BG, BK, VEC, SrcF32> la(SrcF32{Q}, d.r, ti * BG, d.r, kend);
+  LoadXC<BG, BK, VEC, SrcF32> lb(SrcF32{Q}, d.r, tj * BG, d.r, kend);
+  f32x16 acc[Warps<BG, BG>::FM][Warps<BG, BG>::FN];
+  zero_acc(acc);
+  gemm_mainloop<BG, BG, BK>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
+  float* out = reinterpret_cast<float*>(L.ws + d.oS) + static_cast<int64_t>(s) * d.rp * d.rp;
+  store_tile<BG, BG>(out, d.rp, ti * BG, tj * BG, d.r, d.r, acc);
+}
+
+// Q' = Q T^{-1}.  T^{-1} is upper triangular, so output column block tn
+// only needs reduction steps k < (tn + 1) BN.  T^{-1}[k][j] = Y[j][k] with
+// Y = T^{-T} (lower triangular, float64).
+template <int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_trmm(Launch L) {
+  constexpr int BK = 32;
+  __shared__ f32x4 smem[mainloop_cells<BM, BN, BK>()];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int rows = L.which == 0 ? d.m : d.n;
+  const int tm = local / ci.ty, tn = local - tm * ci.ty;
+  const float* Q = qr_source(L, d);
+  float* dst = L.pass == 1 ? reinterpret_cast<float*>(L.ws + d.oB)
+                           : (L.which == 0 ? reinterpret_cast<float*>(L.ws + d.oP) : d.V);
+  const double* Y = reinterpret_cast<const double*>(L.ws + d.oY);
+  const int kend = min(d.r, (tn + 1) * BN);
+  LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{Q}, d.r, tm * BM, rows, kend);
+  LoadKC<BN, BK, true, true, SrcF64> lb(SrcF64{Y}, d.rp, tn * BN, d.r, kend);
+  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
+  zero_acc(acc);
+  gemm_mainloop<BM, BN, BK>(la, lb, 0, (kend + BK - 1) / BK, smem, acc);
+  store_tile<BM, BN>(dst, d.r, tm * BM, tn * BN, rows, d.r, acc);
+}
+
+// Fused weight and residual update over one BM x BN tile of X and R:
+//   X <- X - eta U Vbar^T,   R <- beta ((G + R) - U W^T)
+// Both products share the left operand U; K = r.
+template <typename GT, int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_epi(Launch L) {
+  constexpr int BK = 16;
+  constexpr int CA = TileShape<BM, BK>::CELLS, CB = TileShape<BN, BK>::CELLS;
+  constexpr int STAGE = CA + 2 * CB;
+  __shared__ f32x4 smem[2 * STAGE];
+  using Wp = Warps<BM, BN>;
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int tm = local / ci.ty, tn = local - tm * ci.ty;
+  const float* U = reinterpret_cast<const float*>(L.ws + d.oP);
+  const float* Wf = reinterpret_cast<const float*>(L.ws + d.oW);
+  LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{U}, d.r, tm * BM, d.m, d.r);
+  LoadKC<BN, BK, VEC, false, SrcF32> lv(SrcF32{d.V}, d.r, tn * BN, d.n, d.r);
+  LoadKC<BN, BK, VEC, false, SrcF32> lw(SrcF32{Wf}, d.r, tn * BN, d.n, d.r);
+  f32x16 ax[Wp::FM][Wp::FN], ar[Wp::FM][Wp::FN];
+  zero_acc(ax);
+  zero_acc(ar);
+  const int nk = (d.r + BK - 1) / BK;
+  la.load(0);
+  lv.load(0);
+  lw.load(0);
+  la.store(smem);
+  lv.store(smem + CA);
+  lw.store(smem + CA + CB);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    f32x4* cur = smem + (kt & 1) * STAGE;
+    f32x4* nxt = smem + ((kt & 1) ^ 1) * STAGE;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.load((kt + 1) * BK);
+      lv.load((kt + 1) * BK);
+      lw.load((kt + 1) * BK);
+    }
+    mma_tile<BM, BN, BK>(cur, cur + CA, ax);
+    mma_tile<BM, BN, BK>(cur, cur + CA + CB, ar);
+    if (more) {
+      la.store(nxt);
+      lv.store(nxt + CA);
+      lw.store(nxt + CA + CB);
+    }
+    __syncthreads();
+  }
+  const GT* G = static_cast<const GT*>(d.G);
+  const float eta = L.eta, beta = L.beta;
+#pragma unroll
+  for (int fm = 0; fm < Wp::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < Wp::FN; ++fn) {
+      const int col = tn * BN + acc_col<BM, BN>(fn);
+      if (col >= d.n) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = tm * BM + acc_row<BM, BN>(fm, v);
+        if (row >= d.m) continue;
+        const int64_t o = static_cast<int64_t>(row) * d.n + col;
+        float g;
+        if constexpr (sizeof(GT) == 2) g = bf16_to_f32(G[o]); else g = G[o];
+        const float mv = g + d.R[o];
+        d.X[o] = d.X[o] - eta * ax[fm][fn][v];
+        d.R[o] = beta * (mv - ar[fm][fn][v]);
+      }
+    }
+}
+
+template <class K>
+hipError_t go(K kernel, const Launch& L, hipStream_t st) {
+  if (L.total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(L.total), dim3(kThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st) {
+  if (gdtype == 0) {
+    if (bn == 128) return vec ? go(k_mv<float, 128, true>, L, st) : go(k_mv<float, 128, false>, L, st);
+    return vec ? go(k_mv<float, 64, true>, L, st) : go(k_mv<float, 64, false>, L, st);
+  }
+  if (bn == 128) return vec ? go(k_mv<uint16_t, 128, true>, L, st) : go(k_mv<uint16_t, 128, false>, L, st);
+  return vec ? go(k_mv<uint16_t, 64, true>, L, st) : go(k_mv<uint16_t, 64, false>, L, st);
+}
+
+hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st) {
+  if (gdtype == 0) {
+    if (bn == 128) return vec ? go(k_mtu<float, 128, true>, L, st) : go(k_mtu<float, 128, false>, L, st);
+    return vec ? go(k_mtu<float, 64, true>, L, st) : go(k_mtu<float, 64, false>, L, st);
+  }
+  if (bn == 128) return vec ? go(k_mtu<uint16_t, 128, true>, L, st) : go(k_mtu<uint16_t, 128, false>, L, st);
+  return vec ? go(k_mtu<uint16_t, 64, true>, L, st) : go(k_mtu<uint16_t, 64, false>, L, st);
+}
+
+hipError_t launch_gram(const Launch& L, int bg, bool vec, hipStream_t st) {
+  if (bg == 128) return vec ? go(k_gram<128, true>, L, st) : go(k_gram<128, false>, L, st);
+  return vec ? go(k_gram<64, true>, L, st) : go(k_gram<64, false>, L, st);
+}
+
+hipError_t launch_trmm(const Launch& L, int bn, bool vec, hipStream_t st) {
+  if (bn == 128) return vec ? go(k_trmm<128, true>, L, st) : go(k_trmm<128, false>, L, st);
+  return vec ? go(k_trmm<64, true>, L, st) : go(k_trmm<64, false>, L, st);
+}
+
+hipError_t launch_epi(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st) {
+  if (gdtype == 0) {
+    if (bn == 128) return vec ? go(k_epi<float, 128, true>, L, st) : go(k_epi<float, 128, false>, L, st);
+    return vec ? go(k_epi<float, 64, true>, L, st) : go(k_epi<float, 64, false>, L, st);
+  }
+  if (bn == 128) return vec ? go(k_epi<uint16_t, 128, true>, L, st) : go(k_epi<uint16_t, 128, false>, L, st);
+  return vec ? go(k_epi<uint16_t, 64, true>, L, st) : go(k_epi<uint16_t, 64, false>, L, st);
+}
+
+}  // namespace dion

@@ -1,0 +1,27 @@
+// Host-side launchers of libdion's kernels (one grouped launch each).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "dion_types.h"
+
+namespace dion {
+
+// gdtype: 0 = float32 G, 1 = bfloat16 G.  bn: output tile width (64 or 128).
+// vec: every operand of the launch admits 16-byte vector loads.
+hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st);
+hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st);
+hipError_t launch_gram(const Launch& L, int bg, bool vec, hipStream_t st);
+hipError_t launch_trmm(const Launch& L, int bn, bool vec, hipStream_t st);
+hipError_t launch_epi(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st);
+
+hipError_t launch_chol_init(const Launch& L, hipStream_t st);
+hipError_t launch_chol_diag(const Launch& L, hipStream_t st);
+hipError_t launch_chol_panel(const Launch& L, hipStream_t st);
+hipError_t launch_chol_trail(const Launch& L, hipStream_t st);
+
+hipError_t launch_reduce(const Launch& L, hipStream_t st);
+hipError_t launch_colnorm(const Launch& L, hipStream_t st);
+hipError_t launch_colscale(const Launch& L, hipStream_t st);
+int elems_per_tile();
+
+}  // namespace dion
