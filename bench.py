@@ -1,0 +1,284 @@
+"""Benchmark: Dion / Orth-Dion optimizer steps per second on the 3B-parameter
+Llama-shaped stack (28 layers, 196 matrices: Q/O 3072x3072, K/V 3072x1024,
+gate/up 3072x8192, down 8192x3072; float32 X, R, V; bfloat16 G) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant orth]
+                    [--rank-div 4] [--extra] [--no-cpu]
+
+One step = one grouped libdion step over all 196 matrices (every phase of
+the method).  Inputs are synthetic, drawn on the device before timing.
+Prints one JSON line.  The per-phase durations come from HIP events the
+library records on its own stream during the timed steps; the dominant
+phase (one kernel launch) is reported against the MI355X roofline.  The
+CPU baseline is the float64 oracle on a bounded sample of the same
+workload (one layer), scaled to the whole stack.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12             # MI355X HBM3E bytes/s
+MFMA_F32_PEAK = 157.3e12      # MI355X dense float32 matrix flop/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_epi_llama3b.json")
+KERNEL_SRC = os.path.join(ROOT, "rank_orthonormalized_optimizer_dion_amd", "csrc")
+
+
+def phase_model(mats, variant: str, eg: int):
+    """Algorithmic flops and bytes of each phase, summed over the matrices.
+
+    Per m x n matrix of rank r (eg = bytes per element of G):
+      mv      2mnr flops;  reads G, R, V, writes P: (eg+4)mn + 4nr + 4mr
+      orth_p  CholeskyQR2 of m x r: 4mr^2 + (4/3)r^3; 24mr bytes
+      mtu     2mnr;  reads G, R, U, writes W: (eg+4)mn + 4mr + 4nr
+      right   orth: 4nr^2 + (4/3)r^3, 24nr bytes; dion: 3nr flops, 12nr bytes
+      update  4mnr;  reads X, G, R, U, Vbar, W, writes X, R: (16+eg)mn + 4mr + 8nr
+    """
+    f = dict.fromkeys(("mv", "orth_p", "mtu", "right", "update"), 0.0)
+    b = dict.fromkeys(f, 0.0)
+    for (m, n, r) in mats:
+        mn = m * n
+        f["mv"] += 2.0 * mn * r
+        b["mv"] += (eg + 4) * mn + 4.0 * n * r + 4.0 * m * r
+        f["orth_p"] += 4.0 * m * r * r + 4.0 / 3.0 * r ** 3
+        b["orth_p"] += 24.0 * m * r
+        f["mtu"] += 2.0 * mn * r
+        b["mtu"] += (eg + 4) * mn + 4.0 * m * r + 4.0 * n * r
+        if variant == "orth":
+            f["right"] += 4.0 * n * r * r + 4.0 / 3.0 * r ** 3
+            b["right"] += 24.0 * n * r
+        else:
+            f["right"] += 3.0 * n * r
+            b["right"] += 12.0 * n * r
+        f["update"] += 4.0 * mn * r
+        b["update"] += (16 + eg) * mn + 4.0 * m * r + 8.0 * n * r
+    return f, b
+
+
+def step_model(mats, variant: str, eg: int):
+    """Whole-step algorithmic flops and compulsory bytes (read X, G, R, V;
+    write X, R, V)."""
+    flops = 0.0
+    bmin = 0.0
+    for (m, n, r) in mats:
+        flops += 8.0 * m * n * r + 4.0 * m * r * r + (4.0 * n * r * r if variant == "orth" else 3.0 * n * r)
+        bmin += (16 + eg) * m * n + 8.0 * n * r
+    return flops, bmin
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(KERNEL_SRC)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(KERNEL_SRC, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter runs, or None when missing or taken on other code."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel") != kernel or rec.get("workload") != workload:
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def make_stack(wl, device):
+    from workloads.device import DeviceMatrix
+    out = []
+    for s in wl.mats:
+        out.append(DeviceMatrix(wl, s, device))
+        if s.index % 28 == 27:
+            print(f"[bench]   {s.index + 1} matrices ready", file=sys.stderr, flush=True)
+    return out
+
+
+def time_plan(dion, torch, mats, variant, steps, warmup, eta, beta):
+    plan = dion.Plan([(d.X, d.G, d.R, d.V) for d in mats], variant)
+    ws = plan.new_workspace()
+    for _ in range(warmup):
+        plan.step(eta, beta, ws)
+    torch.cuda.synchronize()
+    plan.timing_enable(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.step(eta, beta, ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    phases, n = plan.timing_read()
+    rc, per = dion.status(ws, plan.count)
+    plan.close()
+    del ws
+    if rc != 0:
+        raise RuntimeError(f"breakdown during the benchmark: {per}")
+    return (t1 - t0) / steps, {k: v / n for k, v in phases.items()}
+
+
+def roofline_of(phase: str, ms: float, f: dict, b: dict, traffic):
+    t = ms * 1e-3
+    intensity = f[phase] / b[phase]
+    if intensity >= MFMA_F32_PEAK / HBM_PEAK:
+        achieved = f[phase] / t / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": 157.3,
+                "unit": "TFLOP/s", "frac": round(achieved / 157.3, 4), "traffic": traffic}
+    achieved = b[phase] / t / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+            "frac": round(achieved / 8000.0, 4), "traffic": traffic}
+
+
+def cpu_baseline(wl, variant: str, layers: int):
+    """The float64 oracle on the first `layers` layer(s) of the stack (one
+    step per matrix, inputs from the seeded numpy streams), scaled to the
+    whole stack."""
+    import numpy as np
+    from oracle import dion_step
+    from workloads import MatrixStream
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    per_layer = sum(1 for s in wl.mats if s.layer == 0)
+    sample = [s for s in wl.mats if s.layer < layers]
+    total = 0.0
+    for s in sample:
+        st = MatrixStream(wl, s)
+        x, r, v = (a.astype(np.float64) for a in st.init())
+        g = st.grad_f64(0)
+        t0 = time.perf_counter()
+        dion_step(x, g, r, v, float(np.float32(wl.eta)), float(np.float32(wl.beta)), variant)
+        total += time.perf_counter() - t0
+    scale = len(wl.mats) / len(sample)
+    return {"value": round(1.0 / (total * scale), 6), "unit": "steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(sample)} of {len(wl.mats)} matrices (layer 0, {per_layer} roles), "
+                      f"one {variant} step each in numpy float64, {total:.1f} s, scaled x{scale:g}"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--variant", choices=("orth", "dion"), default="orth")
+    ap.add_argument("--rank-div", type=int, choices=(4, 16), default=4)
+    ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the other variant and rank fraction")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-layers", type=int, default=1)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (a known byte "
+                         "count for scaling hardware traffic counters)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the Dion step here runs on a single MI355X and "
+              "has no multi-GPU path (how it would shard is described in DESIGN.md).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import rank_orthonormalized_optimizer_dion_amd as dion
+    from workloads import config
+    dion.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    wl = config(4, args.rank_div, layers=args.layers)
+    print(f"[bench] generating {wl.name}: {wl.count} matrices on the device", file=sys.stderr,
+          flush=True)
+    mats = make_stack(wl, dev)
+    torch.cuda.synchronize()
+    print("[bench] inputs ready; timing", file=sys.stderr, flush=True)
+    shapes = [(s.m, s.n, s.r) for s in wl.mats]
+    eg = 2
+    sec, phases = time_plan(dion, torch, mats, args.variant, args.steps, args.warmup,
+                            wl.eta, wl.beta)
+    f, b = phase_model(shapes, args.variant, eg)
+    dom = max(phases, key=phases.get)
+    kernel = {"mv": "k_mv", "orth_p": "orth(P)", "mtu": "k_mtu", "right": "right factor",
+              "update": "k_epi"}[dom]
+    traffic = measured_traffic(kernel, wl.name) if kernel.startswith("k_") else None
+    roof = roofline_of(dom, phases[dom], f, b, traffic)
+    roof["kernel"] = kernel
+    flops, bmin = step_model(shapes, args.variant, eg)
+    t_roof = max(bmin / HBM_PEAK, flops / MFMA_F32_PEAK)
+    out = {
+        "metric": "Dion/Orth-Dion steps/sec + effective HBM GB/s (% roofline), 3B-shaped stack",
+        "value": round(1.0 / sec, 4),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "matrices": wl.count, "variant": args.variant,
+                   "g_dtype": "bf16", "state_dtype": "f32", "layers": args.layers,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "step_roofline": {
+            "bound": "mfma" if flops / MFMA_F32_PEAK > bmin / HBM_PEAK else "hbm",
+            "algorithmic_tflop": round(flops / 1e12, 3),
+            "compulsory_gb": round(bmin / 1e9, 3),
+            "effective_gbps": round(bmin / sec / 1e9, 1),
+            "effective_tflops": round(flops / sec / 1e12, 2),
+            "frac": round(t_roof / sec, 4),
+        },
+        "phase_ms": {k: round(v, 3) for k, v in phases.items()},
+    }
+    if args.extra:
+        extra = {}
+        other = "dion" if args.variant == "orth" else "orth"
+        sec2, ph2 = time_plan(dion, torch, mats, other, max(3, args.steps // 2), 1, wl.eta, wl.beta)
+        extra[f"{other}_r1/{args.rank_div}"] = {"steps_per_s": round(1 / sec2, 4),
+                                                "phase_ms": {k: round(v, 3) for k, v in ph2.items()}}
+        div2 = 16 if args.rank_div == 4 else 4
+        wl2 = config(4, div2, layers=args.layers)
+        for d, s in zip(mats, wl2.mats):
+            d.reset_rank(s.r)
+        torch.cuda.synchronize()
+        for var in ("orth", "dion"):
+            sec3, ph3 = time_plan(dion, torch, mats, var, max(3, args.steps // 2), 1, wl.eta,
+                                  wl.beta)
+            extra[f"{var}_r1/{div2}"] = {"steps_per_s": round(1 / sec3, 4),
+                                         "phase_ms": {k: round(v, 3) for k, v in ph3.items()}}
+        out["extra"] = extra
+    del mats
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.variant, args.cpu_layers)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -143,6 +143,20 @@ int    dion_plan_step(dion_plan* plan, float eta, float beta,
                       void* workspace, size_t workspace_bytes, void* stream);
 void   dion_plan_destroy(dion_plan* plan);
 
+/* Phase timing, for measurement.  A step runs five phases, in order:
+ *   0  P = M V            1  U = orth(P)          2  W = M^T U
+ *   3  Vbar (orth(W) or column normalization)     4  X and R update
+ * dion_plan_timing_enable(plan, max_steps) makes the next max_steps calls of
+ * dion_plan_step record a HIP event at every phase boundary on the step's
+ * stream (creating the events now; 0 disables and frees them).
+ * dion_plan_timing_read waits for the last recorded event, writes the
+ * summed milliseconds of each phase over the recorded steps into
+ * ms_per_phase[DION_PHASES] and the step count into *steps, and starts a
+ * new recording window. */
+#define DION_PHASES 5
+int dion_plan_timing_enable(dion_plan* plan, int max_steps);
+int dion_plan_timing_read(dion_plan* plan, double* ms_per_phase, int* steps);
+
 /* Breakdown check: waits for `stream`, then reads the status words of the
  * last step enqueued on `workspace` (count = 1 for dion_step, the list
  * length for a grouped step).  per_matrix (optional, count ints) receives

@@ -87,6 +87,9 @@ def load() -> ctypes.CDLL:
         "dion_plan_step": (c_int, [vp, c_f, c_f, vp, c_size, vp]),
         "dion_plan_destroy": (None, [vp]),
         "dion_status": (c_int, [vp, c_int, vp, ctypes.POINTER(c_int)]),
+        "dion_plan_timing_enable": (c_int, [vp, c_int]),
+        "dion_plan_timing_read": (c_int, [vp, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -261,6 +264,23 @@ class Plan:
                                       self.workspace_bytes, _stream_handle(stream, self.device))
         if rc != OK:
             raise _err(rc)
+
+    PHASES = ("mv", "orth_p", "mtu", "right", "update")
+
+    def timing_enable(self, max_steps: int) -> None:
+        """Record per-phase HIP events on the next `max_steps` steps."""
+        rc = self._lib.dion_plan_timing_enable(self._h, int(max_steps))
+        if rc != OK:
+            raise _err(rc)
+
+    def timing_read(self):
+        """Wait for the recorded steps; return ({phase: summed ms}, steps)."""
+        ms = (ctypes.c_double * len(self.PHASES))()
+        steps = ctypes.c_int()
+        rc = self._lib.dion_plan_timing_read(self._h, ms, ctypes.byref(steps))
+        if rc != OK:
+            raise _err(rc)
+        return dict(zip(self.PHASES, list(ms))), steps.value
 
     def close(self):
         if getattr(self, "_h", None) is not None:

@@ -11,8 +11,19 @@ namespace dion {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // every kernel runs 4 wavefronts of 64
+
+// Pointers into global memory, so that accesses compile to global_load /
+// global_store (counted by vmcnt only) rather than flat accesses (which also
+// count against lgkmcnt and would make LDS waits wait for HBM).
+template <class T> using gptr = __attribute__((address_space(1))) T*;
+template <class T>
+__device__ __forceinline__ gptr<T> to_global(T* p) {
+  return (gptr<T>)(p);
+}
 
 // Workgroups of a launch are handed to the 8 XCDs round-robin (block b goes
 // to XCD b % 8).  Renumber them so each XCD owns one contiguous range of
@@ -42,60 +53,112 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
 }
 
 // ---------------------------------------------------------------------------
-// Element sources.  ld4 reads 4 consecutive elements (16-byte aligned for
-// float32), ld1 one element; both return float32.
+// Element sources.  A loader keeps what it fetched from global memory in
+// registers in the source's raw form (fetch4: 4 consecutive elements, one
+// vector load; fetch4m: the same with per-element predicates, zero where
+// false), and only converts it to float32 (fin) when it stores the tile to
+// LDS, after the MFMAs of the current tile have been issued, so that the
+// load latency hides behind them.
 struct SrcF32 {
-  const float* p;
-  __device__ __forceinline__ f32x4 ld4(int64_t o) const {
-    return *reinterpret_cast<const f32x4*>(p + o);
+  using Raw = f32x4;
+  gptr<const float> p;
+  __device__ __forceinline__ explicit SrcF32(const float* q) : p(to_global(q)) {}
+  __device__ __forceinline__ Raw fetch4(int64_t o) const {
+    return *(gptr<const f32x4>)(p + o);
   }
-  __device__ __forceinline__ float ld1(int64_t o) const { return p[o]; }
+  __device__ __forceinline__ Raw fetch4m(int64_t o, const bool (&ok)[4]) const {
+    Raw v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = ok[c] ? p[o + c] : 0.0f;
+    return v;
+  }
+  __device__ __forceinline__ static f32x4 fin(const Raw& v) { return v; }
 };
 
 // The buffer M = G + R, formed on the fly (one float32 rounding, the same
 // everywhere it is formed).
 template <typename GT> struct SrcM;
 template <> struct SrcM<float> {
-  const float* g;
-  const float* r;
-  __device__ __forceinline__ f32x4 ld4(int64_t o) const {
-    return *reinterpret_cast<const f32x4*>(g + o) +
-           *reinterpret_cast<const f32x4*>(r + o);
+  struct Raw {
+    f32x4 g, r;
+  };
+  gptr<const float> g;
+  gptr<const float> r;
+  __device__ __forceinline__ SrcM(const float* g_, const float* r_)
+      : g(to_global(g_)), r(to_global(r_)) {}
+  __device__ __forceinline__ Raw fetch4(int64_t o) const {
+    return {*(gptr<const f32x4>)(g + o), *(gptr<const f32x4>)(r + o)};
   }
-  __device__ __forceinline__ float ld1(int64_t o) const { return g[o] + r[o]; }
+  __device__ __forceinline__ Raw fetch4m(int64_t o, const bool (&ok)[4]) const {
+    Raw v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v.g[c] = ok[c] ? g[o + c] : 0.0f;
+      v.r[c] = ok[c] ? r[o + c] : 0.0f;
+    }
+    return v;
+  }
+  __device__ __forceinline__ static f32x4 fin(const Raw& v) { return v.g + v.r; }
 };
 template <> struct SrcM<uint16_t> {
-  const uint16_t* g;
-  const float* r;
-  __device__ __forceinline__ f32x4 ld4(int64_t o) const {
-    const uint2 u = *reinterpret_cast<const uint2*>(g + o);
-    f32x4 a;
-    a[0] = __uint_as_float(u.x << 16);
-    a[1] = __uint_as_float(u.x & 0xffff0000u);
-    a[2] = __uint_as_float(u.y << 16);
-    a[3] = __uint_as_float(u.y & 0xffff0000u);
-    return a + *reinterpret_cast<const f32x4*>(r + o);
+  struct Raw {
+    u32x2 g;
+    f32x4 r;
+  };
+  gptr<const uint16_t> g;
+  gptr<const float> r;
+  __device__ __forceinline__ SrcM(const uint16_t* g_, const float* r_)
+      : g(to_global(g_)), r(to_global(r_)) {}
+  __device__ __forceinline__ Raw fetch4(int64_t o) const {
+    return {*(gptr<const u32x2>)(g + o), *(gptr<const f32x4>)(r + o)};
   }
-  __device__ __forceinline__ float ld1(int64_t o) const {
-    return bf16_to_f32(g[o]) + r[o];
+  __device__ __forceinline__ Raw fetch4m(int64_t o, const bool (&ok)[4]) const {
+    uint32_t h[4];
+    Raw v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      h[c] = ok[c] ? g[o + c] : 0u;
+      v.r[c] = ok[c] ? r[o + c] : 0.0f;
+    }
+    v.g.x = h[0] | (h[1] << 16);
+    v.g.y = h[2] | (h[3] << 16);
+    return v;
+  }
+  __device__ __forceinline__ static f32x4 fin(const Raw& v) {
+    f32x4 a;
+    a[0] = __uint_as_float(v.g.x << 16);
+    a[1] = __uint_as_float(v.g.x & 0xffff0000u);
+    a[2] = __uint_as_float(v.g.y << 16);
+    a[3] = __uint_as_float(v.g.y & 0xffff0000u);
+    return a + v.r;
   }
 };
 
 // float64 source rounded to float32 (the triangular inverse).
 struct SrcF64 {
-  const double* p;
-  __device__ __forceinline__ f32x4 ld4(int64_t o) const {
-    const double2 a = *reinterpret_cast<const double2*>(p + o);
-    const double2 b = *reinterpret_cast<const double2*>(p + o + 2);
-    f32x4 v;
-    v[0] = static_cast<float>(a.x);
-    v[1] = static_cast<float>(a.y);
-    v[2] = static_cast<float>(b.x);
-    v[3] = static_cast<float>(b.y);
+  struct Raw {
+    f64x2 a, b;
+  };
+  gptr<const double> p;
+  __device__ __forceinline__ explicit SrcF64(const double* q) : p(to_global(q)) {}
+  __device__ __forceinline__ Raw fetch4(int64_t o) const {
+    return {*(gptr<const f64x2>)(p + o), *(gptr<const f64x2>)(p + o + 2)};
+  }
+  __device__ __forceinline__ Raw fetch4m(int64_t o, const bool (&ok)[4]) const {
+    Raw v;
+    v.a.x = ok[0] ? p[o] : 0.0;
+    v.a.y = ok[1] ? p[o + 1] : 0.0;
+    v.b.x = ok[2] ? p[o + 2] : 0.0;
+    v.b.y = ok[3] ? p[o + 3] : 0.0;
     return v;
   }
-  __device__ __forceinline__ float ld1(int64_t o) const {
-    return static_cast<float>(p[o]);
+  __device__ __forceinline__ static f32x4 fin(const Raw& v) {
+    f32x4 r;
+    r[0] = static_cast<float>(v.a.x);
+    r[1] = static_cast<float>(v.a.y);
+    r[2] = static_cast<float>(v.b.x);
+    r[3] = static_cast<float>(v.b.y);
+    return r;
   }
 };
 
@@ -118,6 +181,8 @@ template <int BX, int BK> struct TileShape {
 // consecutive float4 (full 128-byte lines for BK = 32).
 // TRI: element is zero when k > x (reading the transpose of a lower
 // triangle).
+// FULL (load): the whole tile lies inside the operand, so loads are
+// unconditional; otherwise every element is bounds-checked.
 template <int BX, int BK, bool VEC, bool TRI, class Src>
 struct LoadKC {
   static constexpr int KQ = BK / 4;
@@ -125,27 +190,28 @@ struct LoadKC {
   static_assert(NV >= 1 && BX * KQ % kThreads == 0, "tile too small");
   Src src;
   int64_t ld;
-  int x0, xmax, kmax;
-  f32x4 v[NV];
+  int x0, xmax, kmax, kcur;
+  typename Src::Raw v[NV];
 
   __device__ __forceinline__ LoadKC(Src s, int64_t ld_, int x0_, int xmax_, int kmax_)
-      : src(s), ld(ld_), x0(x0_), xmax(xmax_), kmax(kmax_) {}
+      : src(s), ld(ld_), x0(x0_), xmax(xmax_), kmax(kmax_), kcur(0) {}
 
+  template <bool FULL>
   __device__ __forceinline__ void load(int k0) {
+    kcur = k0;
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
       const int idx = threadIdx.x + kThreads * s;
       const int kq = idx % KQ, x = idx / KQ;
       const int gx = x0 + x, gk = k0 + 4 * kq;
       const int64_t o = static_cast<int64_t>(gx) * ld + gk;
-      if (VEC && gx < xmax && gk + 3 < kmax && (!TRI || gk + 3 <= gx)) {
-        v[s] = src.ld4(o);
+      if (FULL || (VEC && gx < xmax && gk + 3 < kmax)) {
+        v[s] = src.fetch4(o);
       } else {
+        bool ok[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bool ok = gx < xmax && gk + c < kmax && (!TRI || gk + c <= gx);
-          v[s][c] = ok ? src.ld1(o + c) : 0.0f;
-        }
+        for (int c = 0; c < 4; ++c) ok[c] = gx < xmax && gk + c < kmax;
+        v[s] = src.fetch4m(o, ok);
       }
     }
   }
@@ -154,7 +220,13 @@ struct LoadKC {
     for (int s = 0; s < NV; ++s) {
       const int idx = threadIdx.x + kThreads * s;
       const int kq = idx % KQ, x = idx / KQ;
-      lds[kq * TileShape<BX, BK>::PITCH + x] = v[s];
+      f32x4 val = Src::fin(v[s]);
+      if constexpr (TRI) {
+        const int gx = x0 + x, gk = kcur + 4 * kq;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) val[c] = gk + c <= gx ? val[c] : 0.0f;
+      }
+      lds[kq * TileShape<BX, BK>::PITCH + x] = val;
     }
   }
 };
@@ -170,11 +242,12 @@ struct LoadXC {
   Src src;
   int64_t ld;
   int x0, xmax, kmax;
-  f32x4 v[NPT][4];
+  typename Src::Raw v[NPT][4];
 
   __device__ __forceinline__ LoadXC(Src s, int64_t ld_, int x0_, int xmax_, int kmax_)
       : src(s), ld(ld_), x0(x0_), xmax(xmax_), kmax(kmax_) {}
 
+  template <bool FULL>
   __device__ __forceinline__ void load(int k0) {
 #pragma unroll
     for (int s = 0; s < NPT; ++s) {
@@ -186,12 +259,13 @@ struct LoadXC {
       for (int j = 0; j < 4; ++j) {
         const int gk = k0 + 4 * kg + j;
         const int64_t o = static_cast<int64_t>(gk) * ld + gx;
-        if (VEC && gk < kmax && gx + 3 < xmax) {
-          v[s][j] = src.ld4(o);
+        if (FULL || (VEC && gk < kmax && gx + 3 < xmax)) {
+          v[s][j] = src.fetch4(o);
         } else {
+          bool ok[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            v[s][j][c] = (gk < kmax && gx + c < xmax) ? src.ld1(o + c) : 0.0f;
+          for (int c = 0; c < 4; ++c) ok[c] = gk < kmax && gx + c < xmax;
+          v[s][j] = src.fetch4m(o, ok);
         }
       }
     }
@@ -202,13 +276,16 @@ struct LoadXC {
       const int idx = threadIdx.x + kThreads * s;
       if (NB % kThreads != 0 && idx >= NB) continue;
       const int xq = idx % XQ, kg = idx / XQ;
+      f32x4 w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = Src::fin(v[s][j]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         f32x4 t;
-        t[0] = v[s][0][c];
-        t[1] = v[s][1][c];
-        t[2] = v[s][2][c];
-        t[3] = v[s][3][c];
+        t[0] = w[0][c];
+        t[1] = w[1][c];
+        t[2] = w[2][c];
+        t[3] = w[3][c];
         lds[kg * TileShape<BX, BK>::PITCH + 4 * xq + c] = t;
       }
     }
@@ -281,30 +358,31 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
 // mma_tile consumes it.  One barrier per K tile: the next tile's stores go
 // to the other buffer, which every wavefront finished reading before the
 // previous barrier.
-template <int BM, int BN, int BK, class LA, class LB>
+template <int BM, int BN, int BK, bool FULL, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop(
     LA& la, LB& lb, int kbase, int nk, f32x4* smem,
     f32x16 (&acc)[Warps<BM, BN>::FM][Warps<BM, BN>::FN]) {
   constexpr int CA = TileShape<BM, BK>::CELLS, CB = TileShape<BN, BK>::CELLS;
-  f32x4* sA[2] = {smem, smem + CA + CB};
-  f32x4* sB[2] = {smem + CA, smem + 2 * CA + CB};
+  constexpr int STAGE = CA + CB;
+  // Buffers are addressed by offset from the __shared__ array so that the
+  // compiler keeps LDS addressing (ds_read / ds_write), not flat accesses.
   if (nk <= 0) return;
-  la.load(kbase);
-  lb.load(kbase);
-  la.store(sA[0]);
-  lb.store(sB[0]);
+  la.template load<FULL>(kbase);
+  lb.template load<FULL>(kbase);
+  la.store(smem);
+  lb.store(smem + CA);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+    const int cur = (kt & 1) * STAGE, nxt = STAGE - cur;
     const bool more = kt + 1 < nk;
     if (more) {
-      la.load(kbase + (kt + 1) * BK);
-      lb.load(kbase + (kt + 1) * BK);
+      la.template load<FULL>(kbase + (kt + 1) * BK);
+      lb.template load<FULL>(kbase + (kt + 1) * BK);
     }
-    mma_tile<BM, BN, BK>(sA[cur], sB[cur], acc);
+    mma_tile<BM, BN, BK>(smem + cur, smem + cur + CA, acc);
     if (more) {
-      la.store(sA[cur ^ 1]);
-      lb.store(sB[cur ^ 1]);
+      la.store(smem + nxt);
+      lb.store(smem + nxt + CA);
     }
     __syncthreads();
   }

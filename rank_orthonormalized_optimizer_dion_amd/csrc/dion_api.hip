@@ -65,6 +65,9 @@ struct dion_plan {
   hipEvent_t ev = nullptr;
   bool ev_pending = false;
   std::vector<uint64_t> key;          // cache key (grouped calls)
+  // Phase timing (dion_plan_timing_*): DION_PHASES + 1 events per step.
+  std::vector<hipEvent_t> tev;
+  int t_max = 0, t_count = 0;
 };
 
 namespace dion {
@@ -303,8 +306,16 @@ hipError_t orth(const dion_plan& p, Launch base, int which, hipStream_t st) {
   return hipSuccess;
 }
 
+// Records the phase-boundary event `b` of the current timed step, if any.
+struct Marker {
+  hipEvent_t* ev = nullptr;
+  hipError_t mark(int b, hipStream_t st) const {
+    return ev ? hipEventRecord(ev[b], st) : hipSuccess;
+  }
+};
+
 hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, float beta,
-                    char* ws, hipStream_t st) {
+                    char* ws, hipStream_t st, const Marker& mk = Marker{}) {
   Launch base{};
   base.table = dev_table;
   if (p.single) base.inl = p.table[0];
@@ -315,6 +326,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   const int ept = elems_per_tile();
 
   // P = M V
+  DION_TRY(mk.mark(0, st));
   for (int bn : {128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_r != bn) return false;
@@ -335,7 +347,9 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   }, [&](const Launch& L) { return launch_reduce(L, st); }));
 
   // U = orth(P)
+  DION_TRY(mk.mark(1, st));
   DION_TRY(orth(p, base, 0, st));
+  DION_TRY(mk.mark(2, st));
 
   // W = M^T U
   for (int bn : {128, 64}) {
@@ -358,6 +372,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   }, [&](const Launch& L) { return launch_reduce(L, st); }));
 
   // Vbar into V
+  DION_TRY(mk.mark(3, st));
   if (p.variant == DION_VARIANT_ORTH) {
     DION_TRY(orth(p, base, 1, st));
   } else {
@@ -373,6 +388,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   }
 
   // X and R
+  DION_TRY(mk.mark(4, st));
   for (int bn : {128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_n != bn) return false;
@@ -382,6 +398,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
       return true;
     }, [&](const Launch& L) { return launch_epi(L, p.gdtype, bn, p.vec, st); }));
   }
+  DION_TRY(mk.mark(5, st));
   return hipSuccess;
 }
 
@@ -392,8 +409,18 @@ int check_call(const dion_plan& p, float eta, float beta, const void* ws, size_t
   return DION_OK;
 }
 
+void timing_free(dion_plan* p) {
+  for (hipEvent_t e : p->tev) (void)hipEventDestroy(e);
+  p->tev.clear();
+  p->t_max = p->t_count = 0;
+}
+
 void plan_free(dion_plan* p) {
   if (!p) return;
+  if (!p->tev.empty()) {
+    (void)hipEventSynchronize(p->tev[p->t_count > 0 ? (p->t_count - 1) * (DION_PHASES + 1) + DION_PHASES : 0]);
+    timing_free(p);
+  }
   if (p->ev) {
     if (p->ev_pending) (void)hipEventSynchronize(p->ev);
     (void)hipEventDestroy(p->ev);
@@ -426,7 +453,9 @@ int plan_step(dion_plan* p, float eta, float beta, void* ws, size_t bytes, hipSt
     return DION_ERR_HIP;
   if (hipEventRecord(p->ev, st) != hipSuccess) return DION_ERR_HIP;
   p->ev_pending = true;
-  return run_step(*p, dev_table, eta, beta, w, st) == hipSuccess ? DION_OK : DION_ERR_HIP;
+  Marker mk;
+  if (p->t_count < p->t_max) mk.ev = &p->tev[static_cast<size_t>(p->t_count++) * (DION_PHASES + 1)];
+  return run_step(*p, dev_table, eta, beta, w, st, mk) == hipSuccess ? DION_OK : DION_ERR_HIP;
 }
 
 // Cache of grouped plans keyed by the matrix list (most recent first).
@@ -536,6 +565,50 @@ DION_API int dion_plan_step(dion_plan* plan, float eta, float beta, void* worksp
 }
 
 DION_API void dion_plan_destroy(dion_plan* plan) { plan_free(plan); }
+
+DION_API int dion_plan_timing_enable(dion_plan* plan, int max_steps) {
+  if (!plan || max_steps < 0 || max_steps > (1 << 20)) return DION_ERR_INVALID_ARG;
+  if (!plan->tev.empty()) {
+    if (plan->t_count > 0 &&
+        hipEventSynchronize(plan->tev[(plan->t_count - 1) * (DION_PHASES + 1) + DION_PHASES]) !=
+            hipSuccess)
+      return DION_ERR_HIP;
+    timing_free(plan);
+  }
+  if (max_steps == 0) return DION_OK;
+  plan->tev.resize(static_cast<size_t>(max_steps) * (DION_PHASES + 1), nullptr);
+  for (auto& e : plan->tev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      for (auto& f : plan->tev)
+        if (f) (void)hipEventDestroy(f);
+      plan->tev.clear();
+      return DION_ERR_HIP;
+    }
+  plan->t_max = max_steps;
+  plan->t_count = 0;
+  return DION_OK;
+}
+
+DION_API int dion_plan_timing_read(dion_plan* plan, double* ms_per_phase, int* steps) {
+  if (!plan || !ms_per_phase || !steps) return DION_ERR_INVALID_ARG;
+  for (int ph = 0; ph < DION_PHASES; ++ph) ms_per_phase[ph] = 0.0;
+  *steps = plan->t_count;
+  if (plan->t_count == 0) return DION_OK;
+  const int stride = DION_PHASES + 1;
+  if (hipEventSynchronize(plan->tev[(plan->t_count - 1) * stride + DION_PHASES]) != hipSuccess)
+    return DION_ERR_HIP;
+  for (int s = 0; s < plan->t_count; ++s)
+    for (int ph = 0; ph < DION_PHASES; ++ph) {
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, plan->tev[s * stride + ph], plan->tev[s * stride + ph + 1]) !=
+          hipSuccess)
+        return DION_ERR_HIP;
+      ms_per_phase[ph] += ms;
+    }
+  plan->t_count = 0;
+  return DION_OK;
+}
 
 DION_API int dion_step_batched(const dion_matrix* mats, int count, float eta, float beta,
                                int variant, int g_dtype, void* workspace,

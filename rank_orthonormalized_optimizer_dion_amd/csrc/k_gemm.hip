@@ -15,10 +15,11 @@ namespace {
 constexpr int BM = 128;
 
 template <int TBM, int TBN>
-__device__ __forceinline__ void store_tile(float* out, int64_t ld, int r0, int c0,
+__device__ __forceinline__ void store_tile(float* out_, int64_t ld, int r0, int c0,
                                            int rmax, int cmax,
                                            const f32x16 (&acc)[Warps<TBM, TBN>::FM][Warps<TBM, TBN>::FN]) {
   using W = Warps<TBM, TBN>;
+  gptr<float> out = to_global(out_);
 #pragma unroll
   for (int fm = 0; fm < W::FM; ++fm)
 #pragma unroll
@@ -38,6 +39,22 @@ __device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
 }
 
 // P = (G + R) V over the reduction slice [kbeg, kend) of n.
+template <typename GT, int BN, bool VEC, bool FULL>
+__device__ __forceinline__ void mv_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
+                                        int s, int tm, int tn, int kbeg, int kend, f32x4* smem) {
+  constexpr int BK = 32;
+  LoadKC<BM, BK, VEC, false, SrcM<GT>> la(
+      SrcM<GT>(static_cast<const GT*>(d.G), d.R), d.n, tm * BM, d.m, kend);
+  LoadXC<BN, BK, VEC, SrcF32> lb(SrcF32{d.V}, d.r, tn * BN, d.r, kend);
+  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
+  zero_acc(acc);
+  gemm_mainloop<BM, BN, BK, FULL>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
+  float* out = ci.splits == 1
+                   ? reinterpret_cast<float*>(L.ws + d.oP)
+                   : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.m * d.r;
+  store_tile<BM, BN>(out, d.r, tm * BM, tn * BN, d.m, d.r, acc);
+}
+
 template <typename GT, int BN, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_mv(Launch L) {
   constexpr int BK = 32;
@@ -53,19 +70,29 @@ __global__ __launch_bounds__(kThreads) void k_mv(Launch L) {
   const int tm = rem / ci.ty, tn = rem - tm * ci.ty;
   const int kbeg = s * ci.klen;
   const int kend = min(d.n, kbeg + ci.klen);
-  LoadKC<BM, BK, VEC, false, SrcM<GT>> la(
-      SrcM<GT>{static_cast<const GT*>(d.G), d.R}, d.n, tm * BM, d.m, kend);
-  LoadXC<BN, BK, VEC, SrcF32> lb(SrcF32{d.V}, d.r, tn * BN, d.r, kend);
-  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
-  zero_acc(acc);
-  gemm_mainloop<BM, BN, BK>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
-  float* out = ci.splits == 1
-                   ? reinterpret_cast<float*>(L.ws + d.oP)
-                   : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.m * d.r;
-  store_tile<BM, BN>(out, d.r, tm * BM, tn * BN, d.m, d.r, acc);
+  const bool full = VEC && (tm + 1) * BM <= d.m && (tn + 1) * BN <= d.r && (kend - kbeg) % BK == 0;
+  if (full) mv_body<GT, BN, VEC, true>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+  else mv_body<GT, BN, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
 }
 
 // W = (G + R)^T U over the reduction slice [kbeg, kend) of m.
+template <typename GT, int BN, bool VEC, bool FULL>
+__device__ __forceinline__ void mtu_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
+                                         int s, int tm, int tn, int kbeg, int kend, f32x4* smem) {
+  constexpr int BK = 32;
+  LoadXC<BM, BK, VEC, SrcM<GT>> la(
+      SrcM<GT>(static_cast<const GT*>(d.G), d.R), d.n, tm * BM, d.n, kend);
+  const float* U = reinterpret_cast<const float*>(L.ws + d.oP);
+  LoadXC<BN, BK, VEC, SrcF32> lb(SrcF32{U}, d.r, tn * BN, d.r, kend);
+  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
+  zero_acc(acc);
+  gemm_mainloop<BM, BN, BK, FULL>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
+  float* out = ci.splits == 1
+                   ? reinterpret_cast<float*>(L.ws + d.oW)
+                   : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.n * d.r;
+  store_tile<BM, BN>(out, d.r, tm * BM, tn * BN, d.n, d.r, acc);
+}
+
 template <typename GT, int BN, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_mtu(Launch L) {
   constexpr int BK = 32;
@@ -80,17 +107,9 @@ __global__ __launch_bounds__(kThreads) void k_mtu(Launch L) {
   const int tm = rem / ci.ty, tn = rem - tm * ci.ty;
   const int kbeg = s * ci.klen;
   const int kend = min(d.m, kbeg + ci.klen);
-  LoadXC<BM, BK, VEC, SrcM<GT>> la(
-      SrcM<GT>{static_cast<const GT*>(d.G), d.R}, d.n, tm * BM, d.n, kend);
-  const float* U = reinterpret_cast<const float*>(L.ws + d.oP);
-  LoadXC<BN, BK, VEC, SrcF32> lb(SrcF32{U}, d.r, tn * BN, d.r, kend);
-  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
-  zero_acc(acc);
-  gemm_mainloop<BM, BN, BK>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
-  float* out = ci.splits == 1
-                   ? reinterpret_cast<float*>(L.ws + d.oW)
-                   : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.n * d.r;
-  store_tile<BM, BN>(out, d.r, tm * BM, tn * BN, d.n, d.r, acc);
+  const bool full = VEC && (tm + 1) * BM <= d.n && (tn + 1) * BN <= d.r && (kend - kbeg) % BK == 0;
+  if (full) mtu_body<GT, BN, VEC, true>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+  else mtu_body<GT, BN, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
 }
 
 __device__ __forceinline__ const float* qr_source(const Launch& L, const MatDesc& d) {
@@ -100,6 +119,20 @@ __device__ __forceinline__ const float* qr_source(const Launch& L, const MatDesc
 
 // Partial Gram matrix S_s = Q[kbeg:kend]^T Q[kbeg:kend] on the upper
 // triangle of BG x BG tiles.
+template <int BG, bool VEC, bool FULL>
+__device__ __forceinline__ void gram_body(const Launch& L, const MatDesc& d, int s, int ti, int tj,
+                                          int kbeg, int kend, f32x4* smem) {
+  constexpr int BK = 32;
+  const float* Q = qr_source(L, d);
+  LoadXC<BG, BK, VEC, SrcF32> la(SrcF32{Q}, d.r, ti * BG, d.r, kend);
+  LoadXC<BG, BK, VEC, SrcF32> lb(SrcF32{Q}, d.r, tj * BG, d.r, kend);
+  f32x16 acc[Warps<BG, BG>::FM][Warps<BG, BG>::FN];
+  zero_acc(acc);
+  gemm_mainloop<BG, BG, BK, FULL>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
+  float* out = reinterpret_cast<float*>(L.ws + d.oS) + static_cast<int64_t>(s) * d.rp * d.rp;
+  store_tile<BG, BG>(out, d.rp, ti * BG, tj * BG, d.r, d.r, acc);
+}
+
 template <int BG, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_gram(Launch L) {
   constexpr int BK = 32;
@@ -122,19 +155,31 @@ __global__ __launch_bounds__(kThreads) void k_gram(Launch L) {
   const int tj = ti + p;
   const int kbeg = s * ci.klen;
   const int kend = min(rows, kbeg + ci.klen);
-  const float* Q = qr_source(L, d);
-  LoadXC<BG, BK, VEC, SrcF32> la(SrcF32{Q}, d.r, ti * BG, d.r, kend);
-  LoadXC<BG, BK, VEC, SrcF32> lb(SrcF32{Q}, d.r, tj * BG, d.r, kend);
-  f32x16 acc[Warps<BG, BG>::FM][Warps<BG, BG>::FN];
-  zero_acc(acc);
-  gemm_mainloop<BG, BG, BK>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
-  float* out = reinterpret_cast<float*>(L.ws + d.oS) + static_cast<int64_t>(s) * d.rp * d.rp;
-  store_tile<BG, BG>(out, d.rp, ti * BG, tj * BG, d.r, d.r, acc);
+  const bool full = VEC && (tj + 1) * BG <= d.r && (kend - kbeg) % BK == 0;
+  if (full) gram_body<BG, VEC, true>(L, d, s, ti, tj, kbeg, kend, smem);
+  else gram_body<BG, VEC, false>(L, d, s, ti, tj, kbeg, kend, smem);
 }
 
 // Q' = Q T^{-1}.  T^{-1} is upper triangular, so output column block tn
 // only needs reduction steps k < (tn + 1) BN.  T^{-1}[k][j] = Y[j][k] with
-// Y = T^{-T} (lower triangular, float64).
+// Y = T^{-T} (lower triangular, float64; its strictly upper part is never
+// written and is masked on load).
+template <int BN, bool VEC, bool FULL>
+__device__ __forceinline__ void trmm_body(const Launch& L, const MatDesc& d, int rows, int tm,
+                                          int tn, int kend, f32x4* smem) {
+  constexpr int BK = 32;
+  const float* Q = qr_source(L, d);
+  float* dst = L.pass == 1 ? reinterpret_cast<float*>(L.ws + d.oB)
+                           : (L.which == 0 ? reinterpret_cast<float*>(L.ws + d.oP) : d.V);
+  const double* Y = reinterpret_cast<const double*>(L.ws + d.oY);
+  LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{Q}, d.r, tm * BM, rows, kend);
+  LoadKC<BN, BK, true, true, SrcF64> lb(SrcF64{Y}, d.rp, tn * BN, d.r, kend);
+  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
+  zero_acc(acc);
+  gemm_mainloop<BM, BN, BK, FULL>(la, lb, 0, (kend + BK - 1) / BK, smem, acc);
+  store_tile<BM, BN>(dst, d.r, tm * BM, tn * BN, rows, d.r, acc);
+}
+
 template <int BN, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_trmm(Launch L) {
   constexpr int BK = 32;
@@ -146,35 +191,22 @@ __global__ __launch_bounds__(kThreads) void k_trmm(Launch L) {
   if (skipped(L, d)) return;
   const int rows = L.which == 0 ? d.m : d.n;
   const int tm = local / ci.ty, tn = local - tm * ci.ty;
-  const float* Q = qr_source(L, d);
-  float* dst = L.pass == 1 ? reinterpret_cast<float*>(L.ws + d.oB)
-                           : (L.which == 0 ? reinterpret_cast<float*>(L.ws + d.oP) : d.V);
-  const double* Y = reinterpret_cast<const double*>(L.ws + d.oY);
   const int kend = min(d.r, (tn + 1) * BN);
-  LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{Q}, d.r, tm * BM, rows, kend);
-  LoadKC<BN, BK, true, true, SrcF64> lb(SrcF64{Y}, d.rp, tn * BN, d.r, kend);
-  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
-  zero_acc(acc);
-  gemm_mainloop<BM, BN, BK>(la, lb, 0, (kend + BK - 1) / BK, smem, acc);
-  store_tile<BM, BN>(dst, d.r, tm * BM, tn * BN, rows, d.r, acc);
+  const bool full = VEC && (tm + 1) * BM <= rows && (tn + 1) * BN <= d.r && kend % BK == 0;
+  if (full) trmm_body<BN, VEC, true>(L, d, rows, tm, tn, kend, smem);
+  else trmm_body<BN, VEC, false>(L, d, rows, tm, tn, kend, smem);
 }
 
 // Fused weight and residual update over one BM x BN tile of X and R:
 //   X <- X - eta U Vbar^T,   R <- beta ((G + R) - U W^T)
 // Both products share the left operand U; K = r.
-template <typename GT, int BN, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_epi(Launch L) {
+template <typename GT, int BN, bool VEC, bool FULL>
+__device__ __forceinline__ void epi_body(const Launch& L, const MatDesc& d, int tm, int tn,
+                                         f32x4* smem) {
   constexpr int BK = 16;
   constexpr int CA = TileShape<BM, BK>::CELLS, CB = TileShape<BN, BK>::CELLS;
   constexpr int STAGE = CA + 2 * CB;
-  __shared__ f32x4 smem[2 * STAGE];
   using Wp = Warps<BM, BN>;
-  MatDesc d;
-  ClassInfo ci;
-  int local;
-  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
-  if (skipped(L, d)) return;
-  const int tm = local / ci.ty, tn = local - tm * ci.ty;
   const float* U = reinterpret_cast<const float*>(L.ws + d.oP);
   const float* Wf = reinterpret_cast<const float*>(L.ws + d.oW);
   LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{U}, d.r, tm * BM, d.m, d.r);
@@ -184,21 +216,21 @@ __global__ __launch_bounds__(kThreads) void k_epi(Launch L) {
   zero_acc(ax);
   zero_acc(ar);
   const int nk = (d.r + BK - 1) / BK;
-  la.load(0);
-  lv.load(0);
-  lw.load(0);
+  la.template load<FULL>(0);
+  lv.template load<FULL>(0);
+  lw.template load<FULL>(0);
   la.store(smem);
   lv.store(smem + CA);
   lw.store(smem + CA + CB);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     f32x4* cur = smem + (kt & 1) * STAGE;
-    f32x4* nxt = smem + ((kt & 1) ^ 1) * STAGE;
+    f32x4* nxt = smem + (STAGE - (kt & 1) * STAGE);
     const bool more = kt + 1 < nk;
     if (more) {
-      la.load((kt + 1) * BK);
-      lv.load((kt + 1) * BK);
-      lw.load((kt + 1) * BK);
+      la.template load<FULL>((kt + 1) * BK);
+      lv.template load<FULL>((kt + 1) * BK);
+      lw.template load<FULL>((kt + 1) * BK);
     }
     mma_tile<BM, BN, BK>(cur, cur + CA, ax);
     mma_tile<BM, BN, BK>(cur, cur + CA + CB, ar);
@@ -209,26 +241,44 @@ __global__ __launch_bounds__(kThreads) void k_epi(Launch L) {
     }
     __syncthreads();
   }
-  const GT* G = static_cast<const GT*>(d.G);
+  gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
+  gptr<float> X = to_global(d.X);
+  gptr<float> R = to_global(d.R);
   const float eta = L.eta, beta = L.beta;
 #pragma unroll
   for (int fm = 0; fm < Wp::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < Wp::FN; ++fn) {
       const int col = tn * BN + acc_col<BM, BN>(fn);
-      if (col >= d.n) continue;
+      if (!FULL && col >= d.n) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = tm * BM + acc_row<BM, BN>(fm, v);
-        if (row >= d.m) continue;
+        if (!FULL && row >= d.m) continue;
         const int64_t o = static_cast<int64_t>(row) * d.n + col;
         float g;
         if constexpr (sizeof(GT) == 2) g = bf16_to_f32(G[o]); else g = G[o];
-        const float mv = g + d.R[o];
-        d.X[o] = d.X[o] - eta * ax[fm][fn][v];
-        d.R[o] = beta * (mv - ar[fm][fn][v]);
+        const float mv = g + R[o];
+        X[o] = X[o] - eta * ax[fm][fn][v];
+        R[o] = beta * (mv - ar[fm][fn][v]);
       }
     }
+}
+
+template <typename GT, int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_epi(Launch L) {
+  constexpr int BK = 16;
+  constexpr int STAGE = TileShape<BM, BK>::CELLS + 2 * TileShape<BN, BK>::CELLS;
+  __shared__ f32x4 smem[2 * STAGE];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int tm = local / ci.ty, tn = local - tm * ci.ty;
+  const bool full = VEC && (tm + 1) * BM <= d.m && (tn + 1) * BN <= d.n && d.r % BK == 0;
+  if (full) epi_body<GT, BN, VEC, true>(L, d, tm, tn, smem);
+  else epi_body<GT, BN, VEC, false>(L, d, tm, tn, smem);
 }
 
 template <class K>
