@@ -13,6 +13,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;   // every kernel runs 4 wavefronts of 64
 
@@ -46,6 +47,21 @@ __device__ __forceinline__ void locate(const Launch& L, int t, MatDesc& d,
   const int mi = rel / ci.tiles;
   local = rel - mi * ci.tiles;
   d = L.table ? L.table[ci.first + mi] : L.inl;
+}
+
+// Grouped tile order inside one matrix's tx x ty tile grid: consecutive
+// work items walk down GM tile rows of one tile column before moving to the
+// next column, so the tiles resident at the same time share both operand
+// panels in L2 (about GM row panels and a few column panels).
+__device__ __forceinline__ void tile_order(int local, int tx, int ty, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int per_group = GM * ty;
+  const int g = local / per_group;
+  const int first = g * GM;
+  const int gs = min(tx - first, GM);
+  const int in = local - g * per_group;
+  tm = first + in % gs;
+  tn = in / gs;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
@@ -358,10 +374,8 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
 // mma_tile consumes it.  One barrier per K tile: the next tile's stores go
 // to the other buffer, which every wavefront finished reading before the
 // previous barrier.
-template <int BM, int BN, int BK, bool FULL, class LA, class LB>
-__device__ __forceinline__ void gemm_mainloop(
-    LA& la, LB& lb, int kbase, int nk, f32x4* smem,
-    f32x16 (&acc)[Warps<BM, BN>::FM][Warps<BM, BN>::FN]) {
+template <int BM, int BN, int BK, bool FULL, class LA, class LB, class MMA>
+__device__ __forceinline__ void pipeline(LA& la, LB& lb, int kbase, int nk, f32x4* smem, MMA&& mma) {
   constexpr int CA = TileShape<BM, BK>::CELLS, CB = TileShape<BN, BK>::CELLS;
   constexpr int STAGE = CA + CB;
   // Buffers are addressed by offset from the __shared__ array so that the
@@ -379,12 +393,52 @@ __device__ __forceinline__ void gemm_mainloop(
       la.template load<FULL>(kbase + (kt + 1) * BK);
       lb.template load<FULL>(kbase + (kt + 1) * BK);
     }
-    mma_tile<BM, BN, BK>(smem + cur, smem + cur + CA, acc);
+    mma(smem + cur, smem + cur + CA);
     if (more) {
       la.store(smem + nxt);
       lb.store(smem + nxt + CA);
     }
     __syncthreads();
+  }
+}
+
+template <int BM, int BN, int BK, bool FULL, class LA, class LB>
+__device__ __forceinline__ void gemm_mainloop(
+    LA& la, LB& lb, int kbase, int nk, f32x4* smem,
+    f32x16 (&acc)[Warps<BM, BN>::FM][Warps<BM, BN>::FN]) {
+  pipeline<BM, BN, BK, FULL>(la, lb, kbase, nk, smem, [&](const f32x4* a, const f32x4* b) {
+    mma_tile<BM, BN, BK>(a, b, acc);
+  });
+}
+
+// float64 MFMA on a tile staged as float32 (v_mfma_f64_16x16x4_f64): the
+// float32 products are exact in float64 and the sums are float64.  2 x 2
+// wavefronts, each FB x FB blocks of 16 x 16.  Lane l reads the cell of k
+// group 4q + l/16, row l%16, and feeds its 4 components to 4 MFMAs (the
+// same k order for both operands).
+template <int BG, int BK>
+__device__ __forceinline__ void mma_tile_f64(const f32x4* sA, const f32x4* sB,
+                                             f64x4 (&acc)[BG / 32][BG / 32]) {
+  constexpr int WT = BG / 2, FB = WT / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, i = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int q = 0; q < BK / 16; ++q) {
+    f32x4 a[FB], b[FB];
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      a[f] = sA[(4 * q + grp) * TileShape<BG, BK>::PITCH + wm * WT + f * 16 + i];
+      b[f] = sB[(4 * q + grp) * TileShape<BG, BK>::PITCH + wn * WT + f * 16 + i];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int fm = 0; fm < FB; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FB; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+              static_cast<double>(a[fm][c]), static_cast<double>(b[fn][c]), acc[fm][fn], 0, 0, 0);
   }
 }
 

@@ -4,9 +4,9 @@
 // One step (Orth-Dion page, equation block; Dion's rule from its closing
 // remark) is enqueued as:
 //   k_mv [+k_reduce]                 P = (G + R) V
-//   CholeskyQR2 on P -> U            2 x (k_gram, k_chol_*, k_trmm)
+//   CholeskyQR on P -> U             k_gram (float64), k_chol_*, k_trmm
 //   k_mtu [+k_reduce]                W = (G + R)^T U
-//   Orth-Dion: CholeskyQR2 on W -> V     Dion: k_colnorm, k_colscale -> V
+//   Orth-Dion: CholeskyQR on W -> V      Dion: k_colnorm, k_colscale -> V
 //   k_epi                            X -= eta U V^T, R = beta (G + R - U W^T)
 // Every kernel is one grouped launch over all matrices of the call.
 #include <hip/hip_runtime.h>
@@ -204,9 +204,9 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
       return static_cast<int64_t>(o);
     };
     d.oP = take(m * r * 4);
-    d.oB = take(std::max(m, n) * r * 4);
+    d.oB = take(m * r * 4);
     d.oW = take(n * r * 4);
-    d.oS = take(static_cast<size_t>(std::max(k.s_gp, k.s_gw)) * rp * rp * 4);
+    d.oS = take(static_cast<size_t>(std::max(k.s_gp, k.s_gw)) * rp * rp * 8);
     d.oA = take(rp * rp * 8);
     d.oY = take(rp * rp * 8);
     d.oD = take((kCholNB * kCholNB + rp) * 8);
@@ -251,57 +251,57 @@ hipError_t grouped(const dion_plan& p, const Launch& base, Fill fill, Go go) {
     if (e_ != hipSuccess) return e_;           \
   } while (0)
 
-// CholeskyQR2 of the P (which = 0) or W (which = 1) factor.
+// orth() of the P (which = 0) or W (which = 1) factor by one CholeskyQR
+// pass with a float64 Gram matrix: S = Q^T Q (float64 MFMA), S = T^T T and
+// Y = T^{-T} (float64, blocked), Q T^{-1} (float32 MFMA) into U (oB) or V.
 hipError_t orth(const dion_plan& p, Launch base, int which, hipStream_t st) {
   base.which = which;
+  base.pass = 1;
   base.flag = which == 0 ? DION_STATUS_ORTH_P : DION_STATUS_ORTH_W;
   int max_nblk = 0;
   for (const ClassRec& c : p.cls) max_nblk = std::max(max_nblk, c.rp / kCholNB);
-  for (int pass = 1; pass <= 2; ++pass) {
-    base.pass = pass;
-    for (int bg : {128, 64}) {
-      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-        if (c.bg != bg) return false;
-        const int nt = cdiv(c.r, bg);
-        ci.tx = nt;
-        ci.splits = which == 0 ? c.s_gp : c.s_gw;
-        ci.klen = which == 0 ? c.kl_gp : c.kl_gw;
-        ci.tiles = nt * (nt + 1) / 2 * ci.splits;
-        return true;
-      }, [&](const Launch& L) { return launch_gram(L, bg, p.vec, st); }));
-    }
+  for (int bg : {128, 64}) {
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      if (c.bg != bg) return false;
+      const int nt = cdiv(c.r, bg);
+      ci.tx = nt;
+      ci.splits = which == 0 ? c.s_gp : c.s_gw;
+      ci.klen = which == 0 ? c.kl_gp : c.kl_gw;
+      ci.tiles = nt * (nt + 1) / 2 * ci.splits;
+      return true;
+    }, [&](const Launch& L) { return launch_gram(L, bg, p.vec, st); }));
+  }
+  DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+    const int nb = c.rp / kCholNB;
+    ci.splits = which == 0 ? c.s_gp : c.s_gw;
+    ci.tiles = nb * (nb + 1) / 2;
+    return true;
+  }, [&](const Launch& L) { return launch_chol_init(L, st); }));
+  for (int kb = 0; kb < max_nblk; ++kb) {
+    base.kb = kb;
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      ci.tiles = c.rp / kCholNB > kb ? 1 : 0;
+      return true;
+    }, [&](const Launch& L) { return launch_chol_diag(L, st); }));
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       const int nb = c.rp / kCholNB;
-      ci.splits = which == 0 ? c.s_gp : c.s_gw;
-      ci.tiles = nb * (nb + 1) / 2;
+      ci.tiles = nb > kb ? nb - 1 : 0;
       return true;
-    }, [&](const Launch& L) { return launch_chol_init(L, st); }));
-    for (int kb = 0; kb < max_nblk; ++kb) {
-      base.kb = kb;
-      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-        ci.tiles = c.rp / kCholNB > kb ? 1 : 0;
-        return true;
-      }, [&](const Launch& L) { return launch_chol_diag(L, st); }));
-      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-        const int nb = c.rp / kCholNB;
-        ci.tiles = nb > kb ? nb - 1 : 0;
-        return true;
-      }, [&](const Launch& L) { return launch_chol_panel(L, st); }));
-      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-        const int nl = c.rp / kCholNB - kb - 1;
-        ci.tiles = nl > 0 ? nl * (nl + 1) / 2 + nl * (kb + 1) : 0;
-        return true;
-      }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
-    }
-    for (int bn : {128, 64}) {
-      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-        if (c.bn_r != bn) return false;
-        ci.tx = cdiv(which == 0 ? c.m : c.n, 128);
-        ci.ty = cdiv(c.r, bn);
-        ci.tiles = ci.tx * ci.ty;
-        return true;
-      }, [&](const Launch& L) { return launch_trmm(L, bn, p.vec, st); }));
-    }
+    }, [&](const Launch& L) { return launch_chol_panel(L, st); }));
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      const int nl = c.rp / kCholNB - kb - 1;
+      ci.tiles = nl > 0 ? nl * (nl + 1) / 2 + nl * (kb + 1) : 0;
+      return true;
+    }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
+  }
+  for (int bn : {128, 64}) {
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      if (c.bn_r != bn) return false;
+      ci.tx = cdiv(which == 0 ? c.m : c.n, 128);
+      ci.ty = cdiv(c.r, bn);
+      ci.tiles = ci.tx * ci.ty;
+      return true;
+    }, [&](const Launch& L) { return launch_trmm(L, bn, p.vec, st); }));
   }
   return hipSuccess;
 }

@@ -24,9 +24,9 @@ constexpr int NB = kCholNB;
 constexpr int LP = NB + 1;   // LDS row pitch (doubles)
 
 // A pivot below this fraction of the column's original squared norm means
-// the column is numerically dependent on the previous ones at float32
-// resolution (condition number beyond ~1e3): the factor is declared
-// rank-deficient.
+// the factor's condition number is beyond about 1e3, where the float32
+// product Q T^{-1} would no longer have orthonormal columns to float32
+// accuracy: the factor is declared numerically rank-deficient.
 constexpr double kPivotTol = 1e-6;
 
 __device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
     ++bi;
   }
   const int bj = bi + p;
-  const float* S = reinterpret_cast<const float*>(L.ws + d.oS);
+  const double* S = reinterpret_cast<const double*>(L.ws + d.oS);
   double* A = dptr(L, d.oA);
   double* Sd = dptr(L, d.oD) + NB * NB;
   const int64_t rp = d.rp, plane = rp * rp;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
     double v;
     if (gi < d.r && gj < d.r) {
       v = 0.0;
-      for (int s = 0; s < ci.splits; ++s) v += static_cast<double>(S[s * plane + gi * rp + gj]);
+      for (int s = 0; s < ci.splits; ++s) v += S[s * plane + gi * rp + gj];
     } else {
       v = gi == gj ? 1.0 : 0.0;
     }

@@ -66,8 +66,9 @@ __global__ __launch_bounds__(kThreads) void k_mv(Launch L) {
   // The first kernel of a step clears the matrix's status word.
   if (local == 0 && threadIdx.x == 0) L.status[d.slot] = 0;
   const int per = ci.tx * ci.ty;
-  const int s = local / per, rem = local - s * per;
-  const int tm = rem / ci.ty, tn = rem - tm * ci.ty;
+  const int s = local / per;
+  int tm, tn;
+  tile_order(local - s * per, ci.tx, ci.ty, tm, tn);
   const int kbeg = s * ci.klen;
   const int kend = min(d.n, kbeg + ci.klen);
   const bool full = VEC && (tm + 1) * BM <= d.m && (tn + 1) * BN <= d.r && (kend - kbeg) % BK == 0;
@@ -82,7 +83,7 @@ __device__ __forceinline__ void mtu_body(const Launch& L, const MatDesc& d, cons
   constexpr int BK = 32;
   LoadXC<BM, BK, VEC, SrcM<GT>> la(
       SrcM<GT>(static_cast<const GT*>(d.G), d.R), d.n, tm * BM, d.n, kend);
-  const float* U = reinterpret_cast<const float*>(L.ws + d.oP);
+  const float* U = reinterpret_cast<const float*>(L.ws + d.oB);
   LoadXC<BN, BK, VEC, SrcF32> lb(SrcF32{U}, d.r, tn * BN, d.r, kend);
   f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
   zero_acc(acc);
@@ -103,8 +104,9 @@ __global__ __launch_bounds__(kThreads) void k_mtu(Launch L) {
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
   const int per = ci.tx * ci.ty;
-  const int s = local / per, rem = local - s * per;
-  const int tm = rem / ci.ty, tn = rem - tm * ci.ty;
+  const int s = local / per;
+  int tm, tn;
+  tile_order(local - s * per, ci.tx, ci.ty, tm, tn);
   const int kbeg = s * ci.klen;
   const int kend = min(d.m, kbeg + ci.klen);
   const bool full = VEC && (tm + 1) * BM <= d.n && (tn + 1) * BN <= d.r && (kend - kbeg) % BK == 0;
@@ -112,25 +114,46 @@ __global__ __launch_bounds__(kThreads) void k_mtu(Launch L) {
   else mtu_body<GT, BN, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
 }
 
+// The factor orth() works on: P (which = 0) or W (which = 1).
 __device__ __forceinline__ const float* qr_source(const Launch& L, const MatDesc& d) {
-  const int64_t off = L.pass == 1 ? (L.which == 0 ? d.oP : d.oW) : d.oB;
-  return reinterpret_cast<const float*>(L.ws + off);
+  return reinterpret_cast<const float*>(L.ws + (L.which == 0 ? d.oP : d.oW));
 }
 
 // Partial Gram matrix S_s = Q[kbeg:kend]^T Q[kbeg:kend] on the upper
-// triangle of BG x BG tiles.
+// triangle of BG x BG tiles, in float64: float32 products are exact in
+// float64 and the sums are float64, so S is accurate enough for a single
+// CholeskyQR pass.
 template <int BG, bool VEC, bool FULL>
 __device__ __forceinline__ void gram_body(const Launch& L, const MatDesc& d, int s, int ti, int tj,
                                           int kbeg, int kend, f32x4* smem) {
-  constexpr int BK = 32;
+  constexpr int BK = 32, FB = BG / 32;
   const float* Q = qr_source(L, d);
   LoadXC<BG, BK, VEC, SrcF32> la(SrcF32{Q}, d.r, ti * BG, d.r, kend);
   LoadXC<BG, BK, VEC, SrcF32> lb(SrcF32{Q}, d.r, tj * BG, d.r, kend);
-  f32x16 acc[Warps<BG, BG>::FM][Warps<BG, BG>::FN];
-  zero_acc(acc);
-  gemm_mainloop<BG, BG, BK, FULL>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
-  float* out = reinterpret_cast<float*>(L.ws + d.oS) + static_cast<int64_t>(s) * d.rp * d.rp;
-  store_tile<BG, BG>(out, d.rp, ti * BG, tj * BG, d.r, d.r, acc);
+  f64x4 acc[FB][FB];
+#pragma unroll
+  for (int fm = 0; fm < FB; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FB; ++fn) acc[fm][fn] = f64x4{0.0, 0.0, 0.0, 0.0};
+  pipeline<BG, BG, BK, FULL>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem,
+                             [&](const f32x4* a, const f32x4* b) { mma_tile_f64<BG, BK>(a, b, acc); });
+  gptr<double> out = to_global(reinterpret_cast<double*>(L.ws + d.oS) +
+                               static_cast<int64_t>(s) * d.rp * d.rp);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int fm = 0; fm < FB; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FB; ++fn) {
+      const int col = tj * BG + wn * (BG / 2) + fn * 16 + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        // 16 x 16 float64 MFMA output: lane l, register v holds row
+        // l / 16 + 4 v, column l % 16.
+        const int row = ti * BG + wm * (BG / 2) + fm * 16 + (lane >> 4) + 4 * v;
+        if (FULL || (row < d.r && col < d.r)) out[static_cast<int64_t>(row) * d.rp + col] = acc[fm][fn][v];
+      }
+    }
 }
 
 template <int BG, bool VEC>
@@ -169,8 +192,7 @@ __device__ __forceinline__ void trmm_body(const Launch& L, const MatDesc& d, int
                                           int tn, int kend, f32x4* smem) {
   constexpr int BK = 32;
   const float* Q = qr_source(L, d);
-  float* dst = L.pass == 1 ? reinterpret_cast<float*>(L.ws + d.oB)
-                           : (L.which == 0 ? reinterpret_cast<float*>(L.ws + d.oP) : d.V);
+  float* dst = L.which == 0 ? reinterpret_cast<float*>(L.ws + d.oB) : d.V;
   const double* Y = reinterpret_cast<const double*>(L.ws + d.oY);
   LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{Q}, d.r, tm * BM, rows, kend);
   LoadKC<BN, BK, true, true, SrcF64> lb(SrcF64{Y}, d.rp, tn * BN, d.r, kend);
@@ -190,7 +212,8 @@ __global__ __launch_bounds__(kThreads) void k_trmm(Launch L) {
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
   const int rows = L.which == 0 ? d.m : d.n;
-  const int tm = local / ci.ty, tn = local - tm * ci.ty;
+  int tm, tn;
+  tile_order(local, ci.tx, ci.ty, tm, tn);
   const int kend = min(d.r, (tn + 1) * BN);
   const bool full = VEC && (tm + 1) * BM <= rows && (tn + 1) * BN <= d.r && kend % BK == 0;
   if (full) trmm_body<BN, VEC, true>(L, d, rows, tm, tn, kend, smem);
@@ -207,7 +230,7 @@ __device__ __forceinline__ void epi_body(const Launch& L, const MatDesc& d, int 
   constexpr int CA = TileShape<BM, BK>::CELLS, CB = TileShape<BN, BK>::CELLS;
   constexpr int STAGE = CA + 2 * CB;
   using Wp = Warps<BM, BN>;
-  const float* U = reinterpret_cast<const float*>(L.ws + d.oP);
+  const float* U = reinterpret_cast<const float*>(L.ws + d.oB);
   const float* Wf = reinterpret_cast<const float*>(L.ws + d.oW);
   LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{U}, d.r, tm * BM, d.m, d.r);
   LoadKC<BN, BK, VEC, false, SrcF32> lv(SrcF32{d.V}, d.r, tn * BN, d.n, d.r);
@@ -275,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void k_epi(Launch L) {
   int local;
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
-  const int tm = local / ci.ty, tn = local - tm * ci.ty;
+  int tm, tn;
+  tile_order(local, ci.tx, ci.ty, tm, tn);
   const bool full = VEC && (tm + 1) * BM <= d.m && (tn + 1) * BN <= d.n && d.r % BK == 0;
   if (full) epi_body<GT, BN, VEC, true>(L, d, tm, tn, smem);
   else epi_body<GT, BN, VEC, false>(L, d, tm, tn, smem);
