@@ -27,13 +27,19 @@ __device__ __forceinline__ gptr<T> to_global(T* p) {
 }
 
 // Workgroups of a launch are handed to the 8 XCDs round-robin (block b goes
-// to XCD b % 8).  Renumber them so each XCD owns one contiguous range of
-// logical work items; neighbouring tiles share operands, and each XCD has
-// its own L2.
+// to XCD b % 8), and each XCD has its own L2.  Renumber them so that each
+// XCD works through chunks of kXcdChunk consecutive logical work items
+// (neighbouring tiles share operand panels in that XCD's L2), with the
+// chunks dealt to the XCDs in turn: at any time all XCDs work on nearby
+// chunks, so a launch whose tiles differ in cost (different matrix shapes)
+// stays balanced across XCDs.  Blocks of a last, partial round of chunks
+// keep their own number.  The map is a bijection on [0, nb).
+constexpr int kXcdChunk = 64;
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
-  const int q = nb >> 3, rem = nb & 7;
+  const int round = 8 * kXcdChunk;
+  if (b >= nb / round * round) return b;
   const int x = b & 7, i = b >> 3;
-  return x * q + (x < rem ? x : rem) + i;
+  return ((i / kXcdChunk) * 8 + x) * kXcdChunk + i % kXcdChunk;
 }
 
 // Find the matrix and the local work item of logical item t.
@@ -400,6 +406,53 @@ __device__ __forceinline__ void pipeline(LA& la, LB& lb, int kbase, int nk, f32x
     }
     __syncthreads();
   }
+}
+
+// Three-stage pipeline: LDS holds tile kt (being multiplied) and receives
+// tile kt+1 from one register set while the other register set already has
+// the global loads of tile kt+2 in flight, so every load has two MMA phases
+// to arrive.  Register sets alternate, hence the 2-step unrolled loop.
+template <int BM, int BN, int BK, bool FULL, class LA, class LB, class MMA>
+__device__ __forceinline__ void pipeline2(LA& a0, LA& a1, LB& b0, LB& b1, int kbase, int nk,
+                                          f32x4* smem, MMA&& mma) {
+  constexpr int CA = TileShape<BM, BK>::CELLS, CB = TileShape<BN, BK>::CELLS;
+  constexpr int STAGE = CA + CB;
+  if (nk <= 0) return;
+  a0.template load<FULL>(kbase);
+  b0.template load<FULL>(kbase);
+  if (nk > 1) {
+    a1.template load<FULL>(kbase + BK);
+    b1.template load<FULL>(kbase + BK);
+  }
+  a0.store(smem);
+  b0.store(smem + CA);
+  __syncthreads();
+  const int pairs = nk >> 1;
+  for (int p = 0; p < pairs; ++p) {
+    const int kt = 2 * p;
+    // tile kt is in LDS stage 0; set 1 holds tile kt+1; set 0 takes kt+2
+    const bool more0 = kt + 2 < nk;
+    if (more0) {
+      a0.template load<FULL>(kbase + (kt + 2) * BK);
+      b0.template load<FULL>(kbase + (kt + 2) * BK);
+    }
+    mma(smem, smem + CA);
+    a1.store(smem + STAGE);
+    b1.store(smem + STAGE + CA);
+    __syncthreads();
+    // tile kt+1 is in LDS stage 1; set 0 holds tile kt+2; set 1 takes kt+3
+    if (kt + 3 < nk) {
+      a1.template load<FULL>(kbase + (kt + 3) * BK);
+      b1.template load<FULL>(kbase + (kt + 3) * BK);
+    }
+    mma(smem + STAGE, smem + STAGE + CA);
+    if (more0) {
+      a0.store(smem);
+      b0.store(smem + CA);
+    }
+    __syncthreads();
+  }
+  if (nk & 1) mma(smem, smem + CA);   // last tile, already in stage 0
 }
 
 template <int BM, int BN, int BK, bool FULL, class LA, class LB>

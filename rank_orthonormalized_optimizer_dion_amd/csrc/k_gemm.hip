@@ -43,12 +43,13 @@ template <typename GT, int BN, bool VEC, bool FULL>
 __device__ __forceinline__ void mv_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
                                         int s, int tm, int tn, int kbeg, int kend, f32x4* smem) {
   constexpr int BK = 32;
-  LoadKC<BM, BK, VEC, false, SrcM<GT>> la(
-      SrcM<GT>(static_cast<const GT*>(d.G), d.R), d.n, tm * BM, d.m, kend);
-  LoadXC<BN, BK, VEC, SrcF32> lb(SrcF32{d.V}, d.r, tn * BN, d.r, kend);
+  const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
+  LoadKC<BM, BK, VEC, false, SrcM<GT>> la0(sm, d.n, tm * BM, d.m, kend), la1 = la0;
+  LoadXC<BN, BK, VEC, SrcF32> lb0(SrcF32{d.V}, d.r, tn * BN, d.r, kend), lb1 = lb0;
   f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
   zero_acc(acc);
-  gemm_mainloop<BM, BN, BK, FULL>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
+  pipeline2<BM, BN, BK, FULL>(la0, la1, lb0, lb1, kbeg, (kend - kbeg + BK - 1) / BK, smem,
+                              [&](const f32x4* a, const f32x4* b) { mma_tile<BM, BN, BK>(a, b, acc); });
   float* out = ci.splits == 1
                    ? reinterpret_cast<float*>(L.ws + d.oP)
                    : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.m * d.r;
@@ -81,13 +82,14 @@ template <typename GT, int BN, bool VEC, bool FULL>
 __device__ __forceinline__ void mtu_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
                                          int s, int tm, int tn, int kbeg, int kend, f32x4* smem) {
   constexpr int BK = 32;
-  LoadXC<BM, BK, VEC, SrcM<GT>> la(
-      SrcM<GT>(static_cast<const GT*>(d.G), d.R), d.n, tm * BM, d.n, kend);
+  const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
+  LoadXC<BM, BK, VEC, SrcM<GT>> la0(sm, d.n, tm * BM, d.n, kend), la1 = la0;
   const float* U = reinterpret_cast<const float*>(L.ws + d.oB);
-  LoadXC<BN, BK, VEC, SrcF32> lb(SrcF32{U}, d.r, tn * BN, d.r, kend);
+  LoadXC<BN, BK, VEC, SrcF32> lb0(SrcF32{U}, d.r, tn * BN, d.r, kend), lb1 = lb0;
   f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
   zero_acc(acc);
-  gemm_mainloop<BM, BN, BK, FULL>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem, acc);
+  pipeline2<BM, BN, BK, FULL>(la0, la1, lb0, lb1, kbeg, (kend - kbeg + BK - 1) / BK, smem,
+                              [&](const f32x4* a, const f32x4* b) { mma_tile<BM, BN, BK>(a, b, acc); });
   float* out = ci.splits == 1
                    ? reinterpret_cast<float*>(L.ws + d.oW)
                    : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.n * d.r;
