@@ -38,6 +38,11 @@ constexpr int kBK = 32;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
+// The fused X / R update works on 128 x 64 tiles: its two accumulator sets
+// then leave room for 3 wavefronts per SIMD, so that one block's X, G, R
+// traffic overlaps another block's MFMAs.
+constexpr int kEpiBN = 64;
+
 // Output tile width: 128 unless that wastes more than 10% of the tile.
 int pick_bn(int cols) {
   const int t128 = cdiv(cols, 128) * 128;
@@ -143,7 +148,7 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
       k.r = static_cast<int>(mats[i].r);
       k.rp = cdiv(k.r, kCholNB) * kCholNB;
       k.bn_r = pick_bn(k.r);
-      k.bn_n = pick_bn(k.n);
+      k.bn_n = kEpiBN;
       k.bg = pick_bn(k.r);
       p.cls.push_back(k);
     }
