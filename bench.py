@@ -27,6 +27,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12             # MI355X HBM3E bytes/s
 MFMA_F32_PEAK = 157.3e12      # MI355X dense float32 matrix flop/s
+MFMA_BF16_PEAK = 2516.6e12    # MI355X dense bfloat16 matrix flop/s
+# Matrix-core operations per algorithmic flop of the three m x n x r
+# products: 1 for float32 MFMA, 3 bfloat16 products for split-bfloat16.
+MATH = {"f32": (MFMA_F32_PEAK, 1), "bf16x3": (MFMA_BF16_PEAK, 3)}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_epi_llama3b.json")
 KERNEL_SRC = os.path.join(ROOT, "rank_orthonormalized_optimizer_dion_amd", "csrc")
 
@@ -107,8 +111,8 @@ def make_stack(wl, device):
     return out
 
 
-def time_plan(dion, torch, mats, variant, steps, warmup, eta, beta):
-    plan = dion.Plan([(d.X, d.G, d.R, d.V) for d in mats], variant)
+def time_plan(dion, torch, mats, variant, steps, warmup, eta, beta, math="f32"):
+    plan = dion.Plan([(d.X, d.G, d.R, d.V) for d in mats], variant, math=math)
     ws = plan.new_workspace()
     for _ in range(warmup):
         plan.step(eta, beta, ws)
@@ -129,16 +133,27 @@ def time_plan(dion, torch, mats, variant, steps, warmup, eta, beta):
     return (t1 - t0) / steps, {k: v / n for k, v in phases.items()}
 
 
-def roofline_of(phase: str, ms: float, f: dict, b: dict, traffic):
+def roofline_of(phase: str, ms: float, f: dict, b: dict, traffic, math: str):
+    """Roofline of one phase (one kernel launch on the 3B stack).
+
+    achieved = algorithmic flops (or bytes) / duration, against the
+    published peak of the arithmetic the kernel runs on: float32 MFMA, or
+    bfloat16 MFMA for split-bfloat16 (which issues 3 bfloat16 products per
+    algorithmic flop; the bound is decided on the executed intensity)."""
     t = ms * 1e-3
-    intensity = f[phase] / b[phase]
-    if intensity >= MFMA_F32_PEAK / HBM_PEAK:
+    peak, ops = MATH[math] if phase in ("mv", "mtu", "update") else (MFMA_F32_PEAK, 1)
+    intensity = ops * f[phase] / b[phase]
+    out = {}
+    if intensity >= peak / HBM_PEAK:
         achieved = f[phase] / t / 1e12
-        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": 157.3,
-                "unit": "TFLOP/s", "frac": round(achieved / 157.3, 4), "traffic": traffic}
-    achieved = b[phase] / t / 1e9
-    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-            "frac": round(achieved / 8000.0, 4), "traffic": traffic}
+        out = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak / 1e12, 1),
+               "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4), "traffic": traffic}
+    else:
+        achieved = b[phase] / t / 1e9
+        out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+               "frac": round(achieved / 8000.0, 4), "traffic": traffic}
+    out["mfma_ops_per_flop"] = ops
+    return out
 
 
 def cpu_baseline(wl, variant: str, layers: int):
@@ -177,6 +192,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--variant", choices=("orth", "dion"), default="orth")
+    ap.add_argument("--math", choices=("f32", "bf16x3"), default="bf16x3",
+                    help="arithmetic of the three m x n x r products: split-bfloat16 "
+                         "(default) or float32 MFMA")
     ap.add_argument("--rank-div", type=int, choices=(4, 16), default=4)
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--extra", action="store_true",
@@ -217,16 +235,23 @@ def main(argv=None) -> int:
     shapes = [(s.m, s.n, s.r) for s in wl.mats]
     eg = 2
     sec, phases = time_plan(dion, torch, mats, args.variant, args.steps, args.warmup,
-                            wl.eta, wl.beta)
+                            wl.eta, wl.beta, args.math)
     f, b = phase_model(shapes, args.variant, eg)
     dom = max(phases, key=phases.get)
     kernel = {"mv": "k_mv", "orth_p": "orth(P)", "mtu": "k_mtu", "right": "right factor",
               "update": "k_epi"}[dom]
+    if args.math == "bf16x3" and kernel in ("k_mv", "k_mtu", "k_epi"):
+        kernel += "3"
     traffic = measured_traffic(kernel, wl.name) if kernel.startswith("k_") else None
-    roof = roofline_of(dom, phases[dom], f, b, traffic)
+    roof = roofline_of(dom, phases[dom], f, b, traffic, args.math)
     roof["kernel"] = kernel
     flops, bmin = step_model(shapes, args.variant, eg)
-    t_roof = max(bmin / HBM_PEAK, flops / MFMA_F32_PEAK)
+    # whole-step roofline: the three products at the chosen arithmetic's
+    # peak (ops per flop included), orth at the float32 matrix peak
+    peak, ops = MATH[args.math]
+    f_prod = f["mv"] + f["mtu"] + f["update"]
+    t_mfma = ops * f_prod / peak + (flops - f_prod) / MFMA_F32_PEAK
+    t_roof = max(bmin / HBM_PEAK, t_mfma)
     out = {
         "metric": "Dion/Orth-Dion steps/sec + effective HBM GB/s (% roofline), 3B-shaped stack",
         "value": round(1.0 / sec, 4),
@@ -238,14 +263,15 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16x3" if args.math == "bf16x3" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "matrices": wl.count, "variant": args.variant,
+                   "math": args.math,
                    "g_dtype": "bf16", "state_dtype": "f32", "layers": args.layers,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "step_roofline": {
-            "bound": "mfma" if flops / MFMA_F32_PEAK > bmin / HBM_PEAK else "hbm",
+            "bound": "mfma" if t_mfma > bmin / HBM_PEAK else "hbm",
             "algorithmic_tflop": round(flops / 1e12, 3),
             "compulsory_gb": round(bmin / 1e9, 3),
             "effective_gbps": round(bmin / sec / 1e9, 1),
@@ -256,8 +282,14 @@ def main(argv=None) -> int:
     }
     if args.extra:
         extra = {}
+        other_math = "f32" if args.math == "bf16x3" else "bf16x3"
+        secm, phm = time_plan(dion, torch, mats, args.variant, max(3, args.steps // 2), 1, wl.eta,
+                              wl.beta, other_math)
+        extra[f"{args.variant}_r1/{args.rank_div}_{other_math}"] = {
+            "steps_per_s": round(1 / secm, 4), "phase_ms": {k: round(v, 3) for k, v in phm.items()}}
         other = "dion" if args.variant == "orth" else "orth"
-        sec2, ph2 = time_plan(dion, torch, mats, other, max(3, args.steps // 2), 1, wl.eta, wl.beta)
+        sec2, ph2 = time_plan(dion, torch, mats, other, max(3, args.steps // 2), 1, wl.eta,
+                              wl.beta, args.math)
         extra[f"{other}_r1/{args.rank_div}"] = {"steps_per_s": round(1 / sec2, 4),
                                                 "phase_ms": {k: round(v, 3) for k, v in ph2.items()}}
         div2 = 16 if args.rank_div == 4 else 4
@@ -267,7 +299,7 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         for var in ("orth", "dion"):
             sec3, ph3 = time_plan(dion, torch, mats, var, max(3, args.steps // 2), 1, wl.eta,
-                                  wl.beta)
+                                  wl.beta, args.math)
             extra[f"{var}_r1/{div2}"] = {"steps_per_s": round(1 / sec3, 4),
                                          "phase_ms": {k: round(v, 3) for k, v in ph3.items()}}
         out["extra"] = extra

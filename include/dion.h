@@ -67,6 +67,20 @@ extern "C" {
  * normalization. */
 #define DION_VARIANT_DION 0
 #define DION_VARIANT_ORTH 1
+#define DION_VARIANT_MASK 0xff
+
+/* Arithmetic of the three m x n x r products (P = M V, W = M^T U and the
+ * X / R update), OR-ed into the `variant` argument of every entry point.
+ * DION_MATH_F32 (default): float32 MFMA products, float32 accumulation.
+ * DION_MATH_BF16X3: each float32 operand x is split into bfloat16
+ *   hi = bf16(x) and lo = bf16(x - hi), and a product is taken as
+ *   hi*hi + hi*lo + lo*hi on the bfloat16 matrix cores with float32
+ *   accumulation: relative product error up to 2^-16 instead of 2^-24, at
+ *   about five times the float32 matrix rate.  orth() (the Gram matrix in
+ *   float64, the triangular product in float32) is unaffected. */
+#define DION_MATH_F32     0x000
+#define DION_MATH_BF16X3  0x100
+#define DION_MATH_MASK    0x100
 
 /* Element type of G. */
 #define DION_DTYPE_F32  0

@@ -29,6 +29,7 @@ ERR_HIP = -3
 ERR_BREAKDOWN = -4
 
 VARIANTS = {"dion": 0, "orth": 1}
+MATH = {"f32": 0x000, "bf16x3": 0x100}
 STATUS_ORTH_P, STATUS_ORTH_W, STATUS_COLNORM = 1, 2, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -108,12 +109,18 @@ def _err(code: int) -> DionError:
     return DionError(code, msg)
 
 
-def _variant(v) -> int:
+def _variant(v, math="f32") -> int:
+    """Rule (``"dion"`` / ``"orth"`` or its code) OR-ed with the math mode
+    (``"f32"``: float32 MFMA products; ``"bf16x3"``: split-bfloat16)."""
     if isinstance(v, str):
         if v not in VARIANTS:
             raise ValueError(f"variant must be one of {list(VARIANTS)}")
-        return VARIANTS[v]
-    return int(v)
+        v = VARIANTS[v]
+    if isinstance(math, str):
+        if math not in MATH:
+            raise ValueError(f"math must be one of {list(MATH)}")
+        math = MATH[math]
+    return int(v) | int(math)
 
 
 def _torch():
@@ -155,10 +162,10 @@ def _check(X, G, R, V):
     return m, n, V.shape[1]
 
 
-def workspace_size(m: int, n: int, r: int, variant="orth", g_dtype=None) -> int:
+def workspace_size(m: int, n: int, r: int, variant="orth", g_dtype=None, math="f32") -> int:
     torch = _torch()
     gd = 1 if g_dtype == torch.bfloat16 else 0
-    size = load().dion_workspace_size(m, n, r, _variant(variant), gd)
+    size = load().dion_workspace_size(m, n, r, _variant(variant, math), gd)
     if size == 0:
         raise ValueError("invalid shape or rank")
     return int(size)
@@ -173,7 +180,8 @@ def _workspace(nbytes: int, device, workspace):
     return workspace
 
 
-def step(X, G, R, V, eta: float, beta: float, variant="orth", workspace=None, stream=None):
+def step(X, G, R, V, eta: float, beta: float, variant="orth", workspace=None, stream=None,
+         math="f32"):
     """One step on one matrix, enqueued on `stream` (default: current).
 
     X, R, V (float32) are updated in place; G (float32 or bfloat16) is read.
@@ -181,7 +189,7 @@ def step(X, G, R, V, eta: float, beta: float, variant="orth", workspace=None, st
     ``status``)."""
     m, n, r = _check(X, G, R, V)
     lib = load()
-    gd, var = _gdtype(G), _variant(variant)
+    gd, var = _gdtype(G), _variant(variant, math)
     nbytes = lib.dion_workspace_size(m, n, r, var, gd)
     if nbytes == 0:
         raise _err(ERR_INVALID_ARG)
@@ -210,20 +218,20 @@ def _mat_array(mats: Sequence[Tuple]) -> Tuple[ctypes.Array, int]:
     return arr, gd
 
 
-def workspace_size_batched(mats: Sequence[Tuple], variant="orth") -> int:
+def workspace_size_batched(mats: Sequence[Tuple], variant="orth", math="f32") -> int:
     arr, gd = _mat_array(mats)
-    size = load().dion_workspace_size_batched(arr, len(mats), _variant(variant), gd)
+    size = load().dion_workspace_size_batched(arr, len(mats), _variant(variant, math), gd)
     if size == 0:
         raise _err(ERR_INVALID_ARG)
     return int(size)
 
 
 def step_batched(mats: Sequence[Tuple], eta: float, beta: float, variant="orth",
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, math="f32"):
     """Grouped step over a list of (X, G, R, V) tuples; returns the workspace."""
     arr, gd = _mat_array(mats)
     lib = load()
-    var = _variant(variant)
+    var = _variant(variant, math)
     nbytes = lib.dion_workspace_size_batched(arr, len(mats), var, gd)
     if nbytes == 0:
         raise _err(ERR_INVALID_ARG)
@@ -239,14 +247,15 @@ def step_batched(mats: Sequence[Tuple], eta: float, beta: float, variant="orth",
 class Plan:
     """A grouped step over a fixed list of matrices (dion_plan_*)."""
 
-    def __init__(self, mats: Sequence[Tuple], variant="orth"):
+    def __init__(self, mats: Sequence[Tuple], variant="orth", math="f32"):
         arr, gd = _mat_array(mats)
         self._lib = load()
         self._mats = list(mats)          # keep the tensors alive
         self.count = len(mats)
         self.device = mats[0][0].device
         h = ctypes.c_void_p()
-        rc = self._lib.dion_plan_create(arr, self.count, _variant(variant), gd, ctypes.byref(h))
+        rc = self._lib.dion_plan_create(arr, self.count, _variant(variant, math), gd,
+                                        ctypes.byref(h))
         if rc != OK:
             raise _err(rc)
         self._h = h

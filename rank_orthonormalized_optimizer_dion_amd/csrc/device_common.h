@@ -14,6 +14,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;   // every kernel runs 4 wavefronts of 64
 
@@ -198,6 +201,52 @@ template <int BX, int BK> struct TileShape {
   static constexpr int CELLS = (BK / 4) * PITCH;
 };
 
+// ---------------------------------------------------------------------------
+// Split-bfloat16 tiles (float32 products as three bfloat16 MFMA products).
+// Every float32 value x is stored as hi = bf16(x) and lo = bf16(x - hi)
+// (round to nearest even; x - hi is exact), so x = hi + lo up to 2^-16 |x|,
+// and a product a b is taken as ahi bhi + ahi blo + alo bhi (the dropped
+// alo blo is below 2^-16 |a b|).  bfloat16 products are exact in the
+// float32 accumulators.
+//
+// Layout per plane (hi, lo): cells of 16 bytes = 8 consecutive k of one
+// row x; cell (k8, x) at k8 * PITCH + swz(x).  An MFMA 32x32x16 operand is
+// one ds_read_b128 per lane: lane l reads cell (2q + l/32, x0 + l%32), i.e.
+// k = 16q + 8(l/32) + e for its elements e = 0..7, the same for both
+// operands.  The swizzle x ^ ((x >> 4) & 3) keeps the reads conflict-free
+// and spreads the transposing stores of column-major sources over the
+// banks.
+template <int BX, int BK> struct BfShape {
+  static constexpr int PITCH = BX + 4;           // cells per k8 row
+  static constexpr int CELLS = (BK / 8) * PITCH; // 16-byte cells per plane
+};
+__device__ __forceinline__ int bf_swz(int x) { return x ^ ((x >> 4) & 3); }
+
+__device__ __forceinline__ void bf_split4(const f32x4& v, u32x2& hi, u32x2& lo) {
+  const bf16x2 h01 = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
+  const bf16x2 h23 = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+  const unsigned a = __builtin_bit_cast(unsigned, h01), b = __builtin_bit_cast(unsigned, h23);
+  const float r0 = v[0] - __uint_as_float(a << 16), r1 = v[1] - __uint_as_float(a & 0xffff0000u);
+  const float r2 = v[2] - __uint_as_float(b << 16), r3 = v[3] - __uint_as_float(b & 0xffff0000u);
+  const bf16x2 l01 = {static_cast<__bf16>(r0), static_cast<__bf16>(r1)};
+  const bf16x2 l23 = {static_cast<__bf16>(r2), static_cast<__bf16>(r3)};
+  hi.x = a;
+  hi.y = b;
+  lo.x = __builtin_bit_cast(unsigned, l01);
+  lo.y = __builtin_bit_cast(unsigned, l23);
+}
+
+// Store the quad (x, k = 4kq .. 4kq+3) as half cells of both planes
+// (planes addressed in 8-byte units).
+template <int BX>
+__device__ __forceinline__ void bf_store_quad(u32x2* hi, u32x2* lo, int kq, int x, const f32x4& v) {
+  u32x2 h, l;
+  bf_split4(v, h, l);
+  const int slot = ((kq >> 1) * (BX + 4) + bf_swz(x)) * 2 + (kq & 1);
+  hi[slot] = h;
+  lo[slot] = l;
+}
+
 // Loader for a source whose reduction index is contiguous:
 // element (x, k) = src[x * ld + k].  Each row of the tile is read as BK/4
 // consecutive float4 (full 128-byte lines for BK = 32).
@@ -249,6 +298,22 @@ struct LoadKC {
         for (int c = 0; c < 4; ++c) val[c] = gk + c <= gx ? val[c] : 0.0f;
       }
       lds[kq * TileShape<BX, BK>::PITCH + x] = val;
+    }
+  }
+  // Split-bfloat16 store (see BfShape): each quad of 4 consecutive k is a
+  // half cell of the hi and lo planes.
+  __device__ __forceinline__ void store_bf(u32x2* hi, u32x2* lo) const {
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      const int kq = idx % KQ, x = idx / KQ;
+      f32x4 val = Src::fin(v[s]);
+      if constexpr (TRI) {
+        const int gx = x0 + x, gk = kcur + 4 * kq;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) val[c] = gk + c <= gx ? val[c] : 0.0f;
+      }
+      bf_store_quad<BX>(hi, lo, kq, x, val);
     }
   }
 };
@@ -309,6 +374,26 @@ struct LoadXC {
         t[2] = w[2][c];
         t[3] = w[3][c];
         lds[kg * TileShape<BX, BK>::PITCH + 4 * xq + c] = t;
+      }
+    }
+  }
+  __device__ __forceinline__ void store_bf(u32x2* hi, u32x2* lo) const {
+#pragma unroll
+    for (int s = 0; s < NPT; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      if (NB % kThreads != 0 && idx >= NB) continue;
+      const int xq = idx % XQ, kg = idx / XQ;
+      f32x4 w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = Src::fin(v[s][j]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        f32x4 t;
+        t[0] = w[0][c];
+        t[1] = w[1][c];
+        t[2] = w[2][c];
+        t[3] = w[3][c];
+        bf_store_quad<BX>(hi, lo, kg, 4 * xq + c, t);
       }
     }
   }
@@ -453,6 +538,97 @@ __device__ __forceinline__ void pipeline2(LA& a0, LA& a1, LB& b0, LB& b1, int kb
     __syncthreads();
   }
   if (nk & 1) mma(smem, smem + CA);   // last tile, already in stage 0
+}
+
+// Split-bfloat16 MFMA tile: BM x BN outputs, 2 x 2 wavefronts, each
+// FM x FN blocks of 32 x 32 accumulated with 3 v_mfma_f32_32x32x16_bf16
+// per 16 k (lo hi, hi lo, hi hi).  Planes: A hi, A lo, B hi, B lo.
+template <int BM, int BN, int BK>
+__device__ __forceinline__ void mma_tile_bf3(const u32x4* ah, const u32x4* al, const u32x4* bh,
+                                             const u32x4* bl,
+                                             f32x16 (&acc)[Warps<BM, BN>::FM][Warps<BM, BN>::FN]) {
+  using W = Warps<BM, BN>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, i = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int q = 0; q < BK / 16; ++q) {
+    bf16x8 a_hi[W::FM], a_lo[W::FM], b_hi[W::FN], b_lo[W::FN];
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm) {
+      const int c = (2 * q + h) * BfShape<BM, BK>::PITCH + bf_swz(wm * W::TM + fm * 32 + i);
+      a_hi[fm] = __builtin_bit_cast(bf16x8, ah[c]);
+      a_lo[fm] = __builtin_bit_cast(bf16x8, al[c]);
+    }
+#pragma unroll
+    for (int fn = 0; fn < W::FN; ++fn) {
+      const int c = (2 * q + h) * BfShape<BN, BK>::PITCH + bf_swz(wn * W::TN + fn * 32 + i);
+      b_hi[fn] = __builtin_bit_cast(bf16x8, bh[c]);
+      b_lo[fn] = __builtin_bit_cast(bf16x8, bl[c]);
+    }
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < W::FN; ++fn) {
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo[fm], b_hi[fn], acc[fm][fn], 0, 0, 0);
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], b_lo[fn], acc[fm][fn], 0, 0, 0);
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], b_hi[fn], acc[fm][fn], 0, 0, 0);
+      }
+  }
+}
+
+// LDS bytes of one split-bfloat16 stage (A and B, hi and lo planes).
+template <int BM, int BN, int BK>
+constexpr int bf_stage_cells() {
+  return 2 * (BfShape<BM, BK>::CELLS + BfShape<BN, BK>::CELLS);
+}
+
+// Three-stage pipeline as pipeline2, storing split-bfloat16 planes.
+// smem: 2 stages of bf_stage_cells() 16-byte cells.
+template <int BM, int BN, int BK, bool FULL, class LA, class LB, class MMA>
+__device__ __forceinline__ void pipeline2_bf(LA& a0, LA& a1, LB& b0, LB& b1, int kbase, int nk,
+                                             u32x4* smem, MMA&& mma) {
+  constexpr int CA = BfShape<BM, BK>::CELLS, CB = BfShape<BN, BK>::CELLS;
+  constexpr int STAGE = 2 * (CA + CB);
+  // plane offsets inside a stage: A hi, A lo, B hi, B lo
+  auto store = [&](auto& la, auto& lb, int st) {
+    u32x4* base = smem + st * STAGE;
+    la.store_bf(reinterpret_cast<u32x2*>(base), reinterpret_cast<u32x2*>(base + CA));
+    lb.store_bf(reinterpret_cast<u32x2*>(base + 2 * CA), reinterpret_cast<u32x2*>(base + 2 * CA + CB));
+  };
+  auto compute = [&](int st) {
+    u32x4* base = smem + st * STAGE;
+    mma(base, base + CA, base + 2 * CA, base + 2 * CA + CB);
+  };
+  if (nk <= 0) return;
+  a0.template load<FULL>(kbase);
+  b0.template load<FULL>(kbase);
+  if (nk > 1) {
+    a1.template load<FULL>(kbase + BK);
+    b1.template load<FULL>(kbase + BK);
+  }
+  store(a0, b0, 0);
+  __syncthreads();
+  const int pairs = nk >> 1;
+  for (int p = 0; p < pairs; ++p) {
+    const int kt = 2 * p;
+    const bool more0 = kt + 2 < nk;
+    if (more0) {
+      a0.template load<FULL>(kbase + (kt + 2) * BK);
+      b0.template load<FULL>(kbase + (kt + 2) * BK);
+    }
+    compute(0);
+    store(a1, b1, 1);
+    __syncthreads();
+    if (kt + 3 < nk) {
+      a1.template load<FULL>(kbase + (kt + 3) * BK);
+      b1.template load<FULL>(kbase + (kt + 3) * BK);
+    }
+    compute(1);
+    if (more0) store(a0, b0, 0);
+    __syncthreads();
+  }
+  if (nk & 1) compute(0);
 }
 
 template <int BM, int BN, int BK, bool FULL, class LA, class LB>

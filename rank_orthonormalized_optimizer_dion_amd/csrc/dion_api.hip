@@ -61,6 +61,7 @@ struct ClassRec {
 
 struct dion_plan {
   int count = 0, variant = 0, gdtype = 0;
+  int math = 0;                       // 0: float32 MFMA, 1: split-bfloat16
   bool vec = false;
   bool single = false;
   std::vector<dion::ClassRec> cls;
@@ -123,10 +124,13 @@ void pick_split(int64_t tiles, int K, int& s, int& klen) {
 int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool single,
                dion_plan& p) {
   if (!mats || count < 1) return DION_ERR_INVALID_ARG;
-  if (variant != DION_VARIANT_DION && variant != DION_VARIANT_ORTH) return DION_ERR_INVALID_ARG;
+  if (variant & ~(DION_VARIANT_MASK | DION_MATH_MASK)) return DION_ERR_INVALID_ARG;
+  const int rule = variant & DION_VARIANT_MASK;
+  if (rule != DION_VARIANT_DION && rule != DION_VARIANT_ORTH) return DION_ERR_INVALID_ARG;
   if (gdtype != DION_DTYPE_F32 && gdtype != DION_DTYPE_BF16) return DION_ERR_INVALID_ARG;
   p.count = count;
-  p.variant = variant;
+  p.variant = rule;
+  p.math = (variant & DION_MATH_BF16X3) ? 1 : 0;
   p.gdtype = gdtype;
   p.single = single;
   p.vec = true;
@@ -341,7 +345,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
       ci.klen = c.kl_mv;
       ci.tiles = ci.tx * ci.ty * ci.splits;
       return true;
-    }, [&](const Launch& L) { return launch_mv(L, p.gdtype, bn, p.vec, st); }));
+    }, [&](const Launch& L) { return launch_mv(L, p.gdtype, bn, p.vec, p.math, st); }));
   }
   base.which = 0;
   DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
@@ -366,7 +370,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
       ci.klen = c.kl_mtu;
       ci.tiles = ci.tx * ci.ty * ci.splits;
       return true;
-    }, [&](const Launch& L) { return launch_mtu(L, p.gdtype, bn, p.vec, st); }));
+    }, [&](const Launch& L) { return launch_mtu(L, p.gdtype, bn, p.vec, p.math, st); }));
   }
   base.which = 1;
   DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
@@ -401,7 +405,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
       ci.ty = cdiv(c.n, bn);
       ci.tiles = ci.tx * ci.ty;
       return true;
-    }, [&](const Launch& L) { return launch_epi(L, p.gdtype, bn, p.vec, st); }));
+    }, [&](const Launch& L) { return launch_epi(L, p.gdtype, bn, p.vec, p.math, st); }));
   }
   DION_TRY(mk.mark(5, st));
   return hipSuccess;

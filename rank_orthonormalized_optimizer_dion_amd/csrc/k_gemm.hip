@@ -307,6 +307,175 @@ __global__ __launch_bounds__(kThreads) void k_epi(Launch L) {
   else epi_body<GT, BN, VEC, false>(L, d, tm, tn, smem);
 }
 
+// ---------------------------------------------------------------------------
+// Split-bfloat16 variants of k_mv, k_mtu and k_epi: the same tiles and
+// loaders, with float32 products taken as three bfloat16 MFMA products (see
+// BfShape).  Relative product error <= 2^-16 instead of float32's 2^-24.
+template <typename GT, int BN, bool VEC, bool FULL>
+__device__ __forceinline__ void mv3_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
+                                         int s, int tm, int tn, int kbeg, int kend, u32x4* smem) {
+  constexpr int BK = 32;
+  const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
+  LoadKC<BM, BK, VEC, false, SrcM<GT>> la0(sm, d.n, tm * BM, d.m, kend), la1 = la0;
+  LoadXC<BN, BK, VEC, SrcF32> lb0(SrcF32{d.V}, d.r, tn * BN, d.r, kend), lb1 = lb0;
+  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
+  zero_acc(acc);
+  pipeline2_bf<BM, BN, BK, FULL>(
+      la0, la1, lb0, lb1, kbeg, (kend - kbeg + BK - 1) / BK, smem,
+      [&](const u32x4* ah, const u32x4* al, const u32x4* bh, const u32x4* bl) {
+        mma_tile_bf3<BM, BN, BK>(ah, al, bh, bl, acc);
+      });
+  float* out = ci.splits == 1
+                   ? reinterpret_cast<float*>(L.ws + d.oP)
+                   : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.m * d.r;
+  store_tile<BM, BN>(out, d.r, tm * BM, tn * BN, d.m, d.r, acc);
+}
+
+template <typename GT, int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_mv3(Launch L) {
+  constexpr int BK = 32;
+  __shared__ u32x4 smem[2 * bf_stage_cells<BM, BN, BK>()];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (local == 0 && threadIdx.x == 0) L.status[d.slot] = 0;
+  const int per = ci.tx * ci.ty;
+  const int s = local / per;
+  int tm, tn;
+  tile_order(local - s * per, ci.tx, ci.ty, tm, tn);
+  const int kbeg = s * ci.klen;
+  const int kend = min(d.n, kbeg + ci.klen);
+  const bool full = VEC && (tm + 1) * BM <= d.m && (tn + 1) * BN <= d.r && (kend - kbeg) % BK == 0;
+  if (full) mv3_body<GT, BN, VEC, true>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+  else mv3_body<GT, BN, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+}
+
+template <typename GT, int BN, bool VEC, bool FULL>
+__device__ __forceinline__ void mtu3_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
+                                          int s, int tm, int tn, int kbeg, int kend, u32x4* smem) {
+  constexpr int BK = 32;
+  const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
+  LoadXC<BM, BK, VEC, SrcM<GT>> la0(sm, d.n, tm * BM, d.n, kend), la1 = la0;
+  const float* U = reinterpret_cast<const float*>(L.ws + d.oB);
+  LoadXC<BN, BK, VEC, SrcF32> lb0(SrcF32{U}, d.r, tn * BN, d.r, kend), lb1 = lb0;
+  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
+  zero_acc(acc);
+  pipeline2_bf<BM, BN, BK, FULL>(
+      la0, la1, lb0, lb1, kbeg, (kend - kbeg + BK - 1) / BK, smem,
+      [&](const u32x4* ah, const u32x4* al, const u32x4* bh, const u32x4* bl) {
+        mma_tile_bf3<BM, BN, BK>(ah, al, bh, bl, acc);
+      });
+  float* out = ci.splits == 1
+                   ? reinterpret_cast<float*>(L.ws + d.oW)
+                   : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.n * d.r;
+  store_tile<BM, BN>(out, d.r, tm * BM, tn * BN, d.n, d.r, acc);
+}
+
+template <typename GT, int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_mtu3(Launch L) {
+  constexpr int BK = 32;
+  __shared__ u32x4 smem[2 * bf_stage_cells<BM, BN, BK>()];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int per = ci.tx * ci.ty;
+  const int s = local / per;
+  int tm, tn;
+  tile_order(local - s * per, ci.tx, ci.ty, tm, tn);
+  const int kbeg = s * ci.klen;
+  const int kend = min(d.m, kbeg + ci.klen);
+  const bool full = VEC && (tm + 1) * BM <= d.n && (tn + 1) * BN <= d.r && (kend - kbeg) % BK == 0;
+  if (full) mtu3_body<GT, BN, VEC, true>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+  else mtu3_body<GT, BN, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+}
+
+template <typename GT, int BN, bool VEC, bool FULL>
+__device__ __forceinline__ void epi3_body(const Launch& L, const MatDesc& d, int tm, int tn,
+                                          u32x4* smem) {
+  constexpr int BK = 32;
+  constexpr int CA = BfShape<BM, BK>::CELLS, CB = BfShape<BN, BK>::CELLS;
+  constexpr int STAGE = 2 * (CA + 2 * CB);
+  using Wp = Warps<BM, BN>;
+  const float* U = reinterpret_cast<const float*>(L.ws + d.oB);
+  const float* Wf = reinterpret_cast<const float*>(L.ws + d.oW);
+  LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{U}, d.r, tm * BM, d.m, d.r);
+  LoadKC<BN, BK, VEC, false, SrcF32> lv(SrcF32{d.V}, d.r, tn * BN, d.n, d.r);
+  LoadKC<BN, BK, VEC, false, SrcF32> lw(SrcF32{Wf}, d.r, tn * BN, d.n, d.r);
+  f32x16 ax[Wp::FM][Wp::FN], ar[Wp::FM][Wp::FN];
+  zero_acc(ax);
+  zero_acc(ar);
+  // stage layout: A hi, A lo, V hi, V lo, W hi, W lo
+  auto store = [&](int st) {
+    u32x4* b = smem + st * STAGE;
+    la.store_bf(reinterpret_cast<u32x2*>(b), reinterpret_cast<u32x2*>(b + CA));
+    lv.store_bf(reinterpret_cast<u32x2*>(b + 2 * CA), reinterpret_cast<u32x2*>(b + 2 * CA + CB));
+    lw.store_bf(reinterpret_cast<u32x2*>(b + 2 * CA + 2 * CB),
+                reinterpret_cast<u32x2*>(b + 2 * CA + 3 * CB));
+  };
+  const int nk = (d.r + BK - 1) / BK;
+  la.template load<FULL>(0);
+  lv.template load<FULL>(0);
+  lw.template load<FULL>(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.template load<FULL>((kt + 1) * BK);
+      lv.template load<FULL>((kt + 1) * BK);
+      lw.template load<FULL>((kt + 1) * BK);
+    }
+    u32x4* b = smem + cur * STAGE;
+    mma_tile_bf3<BM, BN, BK>(b, b + CA, b + 2 * CA, b + 2 * CA + CB, ax);
+    mma_tile_bf3<BM, BN, BK>(b, b + CA, b + 2 * CA + 2 * CB, b + 2 * CA + 3 * CB, ar);
+    if (more) store(cur ^ 1);
+    __syncthreads();
+  }
+  gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
+  gptr<float> X = to_global(d.X);
+  gptr<float> R = to_global(d.R);
+  const float eta = L.eta, beta = L.beta;
+#pragma unroll
+  for (int fm = 0; fm < Wp::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < Wp::FN; ++fn) {
+      const int col = tn * BN + acc_col<BM, BN>(fn);
+      if (!FULL && col >= d.n) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = tm * BM + acc_row<BM, BN>(fm, v);
+        if (!FULL && row >= d.m) continue;
+        const int64_t o = static_cast<int64_t>(row) * d.n + col;
+        float g;
+        if constexpr (sizeof(GT) == 2) g = bf16_to_f32(G[o]); else g = G[o];
+        const float mv = g + R[o];
+        X[o] = X[o] - eta * ax[fm][fn][v];
+        R[o] = beta * (mv - ar[fm][fn][v]);
+      }
+    }
+}
+
+template <typename GT, int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_epi3(Launch L) {
+  constexpr int BK = 32;
+  constexpr int STAGE = 2 * (BfShape<BM, BK>::CELLS + 2 * BfShape<BN, BK>::CELLS);
+  __shared__ u32x4 smem[2 * STAGE];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  int tm, tn;
+  tile_order(local, ci.tx, ci.ty, tm, tn);
+  const bool full = VEC && (tm + 1) * BM <= d.m && (tn + 1) * BN <= d.n && d.r % BK == 0;
+  if (full) epi3_body<GT, BN, VEC, true>(L, d, tm, tn, smem);
+  else epi3_body<GT, BN, VEC, false>(L, d, tm, tn, smem);
+}
+
 template <class K>
 hipError_t go(K kernel, const Launch& L, hipStream_t st) {
   if (L.total <= 0) return hipSuccess;
@@ -316,22 +485,23 @@ hipError_t go(K kernel, const Launch& L, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st) {
-  if (gdtype == 0) {
-    if (bn == 128) return vec ? go(k_mv<float, 128, true>, L, st) : go(k_mv<float, 128, false>, L, st);
-    return vec ? go(k_mv<float, 64, true>, L, st) : go(k_mv<float, 64, false>, L, st);
-  }
-  if (bn == 128) return vec ? go(k_mv<uint16_t, 128, true>, L, st) : go(k_mv<uint16_t, 128, false>, L, st);
-  return vec ? go(k_mv<uint16_t, 64, true>, L, st) : go(k_mv<uint16_t, 64, false>, L, st);
+#define DION_PICK(K, GT, BNV, VECV) \
+  (math ? go(K##3<GT, BNV, VECV>, L, st) : go(K<GT, BNV, VECV>, L, st))
+
+#define DION_DISPATCH(K)                                                         \
+  if (gdtype == 0) {                                                             \
+    if (bn == 128) return vec ? DION_PICK(K, float, 128, true) : DION_PICK(K, float, 128, false); \
+    return vec ? DION_PICK(K, float, 64, true) : DION_PICK(K, float, 64, false);  \
+  }                                                                              \
+  if (bn == 128) return vec ? DION_PICK(K, uint16_t, 128, true) : DION_PICK(K, uint16_t, 128, false); \
+  return vec ? DION_PICK(K, uint16_t, 64, true) : DION_PICK(K, uint16_t, 64, false);
+
+hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st) {
+  DION_DISPATCH(k_mv)
 }
 
-hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st) {
-  if (gdtype == 0) {
-    if (bn == 128) return vec ? go(k_mtu<float, 128, true>, L, st) : go(k_mtu<float, 128, false>, L, st);
-    return vec ? go(k_mtu<float, 64, true>, L, st) : go(k_mtu<float, 64, false>, L, st);
-  }
-  if (bn == 128) return vec ? go(k_mtu<uint16_t, 128, true>, L, st) : go(k_mtu<uint16_t, 128, false>, L, st);
-  return vec ? go(k_mtu<uint16_t, 64, true>, L, st) : go(k_mtu<uint16_t, 64, false>, L, st);
+hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st) {
+  DION_DISPATCH(k_mtu)
 }
 
 hipError_t launch_gram(const Launch& L, int bg, bool vec, hipStream_t st) {
@@ -344,13 +514,8 @@ hipError_t launch_trmm(const Launch& L, int bn, bool vec, hipStream_t st) {
   return vec ? go(k_trmm<64, true>, L, st) : go(k_trmm<64, false>, L, st);
 }
 
-hipError_t launch_epi(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st) {
-  if (gdtype == 0) {
-    if (bn == 128) return vec ? go(k_epi<float, 128, true>, L, st) : go(k_epi<float, 128, false>, L, st);
-    return vec ? go(k_epi<float, 64, true>, L, st) : go(k_epi<float, 64, false>, L, st);
-  }
-  if (bn == 128) return vec ? go(k_epi<uint16_t, 128, true>, L, st) : go(k_epi<uint16_t, 128, false>, L, st);
-  return vec ? go(k_epi<uint16_t, 64, true>, L, st) : go(k_epi<uint16_t, 64, false>, L, st);
+hipError_t launch_epi(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st) {
+  DION_DISPATCH(k_epi)
 }
 
 }  // namespace dion

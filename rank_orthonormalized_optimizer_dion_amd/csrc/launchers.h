@@ -8,11 +8,12 @@ namespace dion {
 
 // gdtype: 0 = float32 G, 1 = bfloat16 G.  bn: output tile width (64 or 128).
 // vec: every operand of the launch admits 16-byte vector loads.
-hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st);
-hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st);
+// math: 0 = float32 MFMA products, 1 = split-bfloat16 (three bf16 MFMAs).
+hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st);
+hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st);
 hipError_t launch_gram(const Launch& L, int bg, bool vec, hipStream_t st);
 hipError_t launch_trmm(const Launch& L, int bn, bool vec, hipStream_t st);
-hipError_t launch_epi(const Launch& L, int gdtype, int bn, bool vec, hipStream_t st);
+hipError_t launch_epi(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st);
 
 hipError_t launch_chol_init(const Launch& L, hipStream_t st);
 hipError_t launch_chol_diag(const Launch& L, hipStream_t st);

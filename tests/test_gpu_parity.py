@@ -34,12 +34,13 @@ def test_config1_one_step(gpu_lib, variant):
 
 
 @pytest.mark.parametrize("variant", [ORTH, DION])
-def test_config1_ten_steps(gpu_lib, variant):
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+def test_config1_ten_steps(gpu_lib, variant, arith):
     wl = config(1)
     c = Case(wl, wl.mats[0])
     for t in range(wl.steps):
         c.load_grad(t)
-        gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant)
+        gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant, math=arith)
         _, x_prev = c.oracle(variant)
         assert_close(c.errors(x_prev), TOL_LONG if t else TOL_1, f"config1 {variant} step {t}")
 
@@ -53,12 +54,13 @@ SHAPES = [
 @pytest.mark.parametrize("m,n,r", SHAPES)
 @pytest.mark.parametrize("variant", [ORTH, DION])
 @pytest.mark.parametrize("g_dtype", ["f32", "bf16"])
-def test_ragged_shapes(gpu_lib, m, n, r, variant, g_dtype):
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+def test_ragged_shapes(gpu_lib, m, n, r, variant, g_dtype, arith):
     wl = _wl(m, n, r, g_dtype)
     c = Case(wl, wl.mats[0])
     c.load_grad(0)
-    say(f"ragged {m}x{n} r={r} {variant} {g_dtype}")
-    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant)
+    say(f"ragged {m}x{n} r={r} {variant} {g_dtype} {arith}")
+    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant, math=arith)
     res, x_prev = c.oracle(variant)
     assert_close(c.errors(x_prev, res.M), TOL_1, f"{m}x{n} r={r} {variant} {g_dtype}")
 
@@ -76,36 +78,40 @@ def test_nonzero_residual_and_second_step(gpu_lib, variant):
 
 
 @pytest.mark.parametrize("variant", [ORTH, DION])
-def test_config2_one_step(gpu_lib, variant):
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+def test_config2_one_step(gpu_lib, variant, arith):
     wl = config(2)
     c = Case(wl, wl.mats[0])
     c.load_grad(0)
-    say(f"config2 {variant} one step")
-    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant)
+    say(f"config2 {variant} {arith} one step")
+    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant, math=arith)
     _, x_prev = c.oracle(variant)
     assert_close(c.errors(x_prev), TOL_1, f"config2 {variant}")
 
 
-def test_config5_r512_one_step(gpu_lib):
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+def test_config5_r512_one_step(gpu_lib, arith):
     wl = config(5, r=512)
     c = Case(wl, wl.mats[0])
     c.load_grad(0)
-    say("config5 r=512 orth one step")
-    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, ORTH)
+    say(f"config5 r=512 orth {arith} one step")
+    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, ORTH, math=arith)
     _, x_prev = c.oracle(ORTH)
     assert_close(c.errors(x_prev), TOL_1, "config5 r=512")
 
 
-def test_batched_config3_stack(gpu_lib):
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+def test_batched_config3_stack(gpu_lib, arith):
     # All 72 matrices of the 160M stack in one grouped call.
     wl = config(3)
     cases = [Case(wl, s) for s in wl.mats]
     for c in cases:
         c.load_grad(0)
     for variant in (ORTH, DION):
-        say(f"config3 stack {variant}")
+        say(f"config3 stack {variant} {arith}")
         state = [(c.X.clone(), c.R.clone(), c.V.clone()) for c in cases]
-        gpu_lib.step_batched([(c.X, c.G, c.R, c.V) for c in cases], wl.eta, wl.beta, variant)
+        gpu_lib.step_batched([(c.X, c.G, c.R, c.V) for c in cases], wl.eta, wl.beta, variant,
+                             math=arith)
         worst = {}
         for c, (x0, r0, v0) in zip(cases, state):
             res = oracle_step(c.x, c.g, c.r, c.v, f32(wl.eta), f32(wl.beta), variant)
