@@ -31,7 +31,7 @@ MFMA_BF16_PEAK = 2516.6e12    # MI355X dense bfloat16 matrix flop/s
 # Matrix-core operations per algorithmic flop of the three m x n x r
 # products: 1 for float32 MFMA, 3 bfloat16 products for split-bfloat16.
 MATH = {"f32": (MFMA_F32_PEAK, 1), "bf16x3": (MFMA_BF16_PEAK, 3)}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_epi_llama3b.json")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "rank_orthonormalized_optimizer_dion_amd", "csrc")
 
 
@@ -40,9 +40,10 @@ def phase_model(mats, variant: str, eg: int):
 
     Per m x n matrix of rank r (eg = bytes per element of G):
       mv      2mnr flops;  reads G, R, V, writes P: (eg+4)mn + 4nr + 4mr
-      orth_p  CholeskyQR2 of m x r: 4mr^2 + (4/3)r^3; 24mr bytes
+      orth_p  CholeskyQR of m x r (Gram, Cholesky and inverse, Q T^-1):
+              4mr^2 + (4/3)r^3; reads P twice, writes U: 12mr bytes
       mtu     2mnr;  reads G, R, U, writes W: (eg+4)mn + 4mr + 4nr
-      right   orth: 4nr^2 + (4/3)r^3, 24nr bytes; dion: 3nr flops, 12nr bytes
+      right   orth: 4nr^2 + (4/3)r^3, 12nr bytes; dion: 3nr flops, 12nr bytes
       update  4mnr;  reads X, G, R, U, Vbar, W, writes X, R: (16+eg)mn + 4mr + 8nr
     """
     f = dict.fromkeys(("mv", "orth_p", "mtu", "right", "update"), 0.0)
@@ -52,12 +53,12 @@ def phase_model(mats, variant: str, eg: int):
         f["mv"] += 2.0 * mn * r
         b["mv"] += (eg + 4) * mn + 4.0 * n * r + 4.0 * m * r
         f["orth_p"] += 4.0 * m * r * r + 4.0 / 3.0 * r ** 3
-        b["orth_p"] += 24.0 * m * r
+        b["orth_p"] += 12.0 * m * r
         f["mtu"] += 2.0 * mn * r
         b["mtu"] += (eg + 4) * mn + 4.0 * m * r + 4.0 * n * r
         if variant == "orth":
             f["right"] += 4.0 * n * r * r + 4.0 / 3.0 * r ** 3
-            b["right"] += 24.0 * n * r
+            b["right"] += 12.0 * n * r
         else:
             f["right"] += 3.0 * n * r
             b["right"] += 12.0 * n * r
@@ -88,9 +89,10 @@ def kernel_source_hash() -> str:
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 counter runs, or None when missing or taken on other code."""
+    rocprofv3 counter runs (profiles/traffic_<kernel>_llama3b.json), or None
+    when missing or taken on other kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(os.path.join(PROFILES, f"traffic_{kernel}_llama3b.json")) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None

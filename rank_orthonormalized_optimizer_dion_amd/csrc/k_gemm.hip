@@ -401,40 +401,52 @@ __device__ __forceinline__ void epi3_body(const Launch& L, const MatDesc& d, int
   using Wp = Warps<BM, BN>;
   const float* U = reinterpret_cast<const float*>(L.ws + d.oB);
   const float* Wf = reinterpret_cast<const float*>(L.ws + d.oW);
-  LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{U}, d.r, tm * BM, d.m, d.r);
-  LoadKC<BN, BK, VEC, false, SrcF32> lv(SrcF32{d.V}, d.r, tn * BN, d.n, d.r);
-  LoadKC<BN, BK, VEC, false, SrcF32> lw(SrcF32{Wf}, d.r, tn * BN, d.n, d.r);
+  LoadKC<BM, BK, VEC, false, SrcF32> la0(SrcF32{U}, d.r, tm * BM, d.m, d.r), la1 = la0;
+  LoadKC<BN, BK, VEC, false, SrcF32> lv0(SrcF32{d.V}, d.r, tn * BN, d.n, d.r), lv1 = lv0;
+  LoadKC<BN, BK, VEC, false, SrcF32> lw0(SrcF32{Wf}, d.r, tn * BN, d.n, d.r), lw1 = lw0;
   f32x16 ax[Wp::FM][Wp::FN], ar[Wp::FM][Wp::FN];
   zero_acc(ax);
   zero_acc(ar);
-  // stage layout: A hi, A lo, V hi, V lo, W hi, W lo
-  auto store = [&](int st) {
+  // stage layout: A hi, A lo, V hi, V lo, W hi, W lo.  Three-stage pipeline:
+  // LDS holds tile kt, one register set tile kt+1, the other has tile
+  // kt+2's loads in flight (the operands are read from L2, and one tile of
+  // split-bfloat16 MFMAs is too short to hide that latency).
+  auto store = [&](auto& la, auto& lv, auto& lw, int st) {
     u32x4* b = smem + st * STAGE;
     la.store_bf(reinterpret_cast<u32x2*>(b), reinterpret_cast<u32x2*>(b + CA));
     lv.store_bf(reinterpret_cast<u32x2*>(b + 2 * CA), reinterpret_cast<u32x2*>(b + 2 * CA + CB));
     lw.store_bf(reinterpret_cast<u32x2*>(b + 2 * CA + 2 * CB),
                 reinterpret_cast<u32x2*>(b + 2 * CA + 3 * CB));
   };
-  const int nk = (d.r + BK - 1) / BK;
-  la.template load<FULL>(0);
-  lv.template load<FULL>(0);
-  lw.template load<FULL>(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.template load<FULL>((kt + 1) * BK);
-      lv.template load<FULL>((kt + 1) * BK);
-      lw.template load<FULL>((kt + 1) * BK);
-    }
-    u32x4* b = smem + cur * STAGE;
+  auto load = [&](auto& la, auto& lv, auto& lw, int k0) {
+    la.template load<FULL>(k0);
+    lv.template load<FULL>(k0);
+    lw.template load<FULL>(k0);
+  };
+  auto compute = [&](int st) {
+    u32x4* b = smem + st * STAGE;
     mma_tile_bf3<BM, BN, BK>(b, b + CA, b + 2 * CA, b + 2 * CA + CB, ax);
     mma_tile_bf3<BM, BN, BK>(b, b + CA, b + 2 * CA + 2 * CB, b + 2 * CA + 3 * CB, ar);
-    if (more) store(cur ^ 1);
+  };
+  const int nk = (d.r + BK - 1) / BK;
+  load(la0, lv0, lw0, 0);
+  if (nk > 1) load(la1, lv1, lw1, BK);
+  store(la0, lv0, lw0, 0);
+  __syncthreads();
+  const int pairs = nk >> 1;
+  for (int p = 0; p < pairs; ++p) {
+    const int kt = 2 * p;
+    const bool more0 = kt + 2 < nk;
+    if (more0) load(la0, lv0, lw0, (kt + 2) * BK);
+    compute(0);
+    store(la1, lv1, lw1, 1);
+    __syncthreads();
+    if (kt + 3 < nk) load(la1, lv1, lw1, (kt + 3) * BK);
+    compute(1);
+    if (more0) store(la0, lv0, lw0, 0);
     __syncthreads();
   }
+  if (nk & 1) compute(0);
   gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
   gptr<float> X = to_global(d.X);
   gptr<float> R = to_global(d.R);
