@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -78,10 +79,18 @@ def step_model(mats, variant: str, eg: int):
     return flops, bmin
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources that define and launch `kernel`: the headers, the
+    host API and the kernel's own translation unit (the other kernel files
+    do not change its code or its launches)."""
+    files = sorted(os.listdir(KERNEL_SRC))
+    units = [f for f in files if f.startswith("k_") and f.endswith(".hip")]
+    own = [f for f in units
+           if re.search(r"\bvoid\s+%s\s*\(" % re.escape(kernel),
+                        open(os.path.join(KERNEL_SRC, f)).read())]
     h = hashlib.sha256()
-    for f in sorted(os.listdir(KERNEL_SRC)):
-        if f.endswith((".hip", ".h")):
+    for f in files:
+        if f.endswith((".hip", ".h")) and (f not in units or f in own):
             with open(os.path.join(KERNEL_SRC, f), "rb") as fh:
                 h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -98,7 +107,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
     if rec.get("kernel") != kernel or rec.get("workload") != workload:
         return None
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 

@@ -47,6 +47,49 @@ __device__ __forceinline__ void load_block(double (*dst)[LP], const double* src,
   }
 }
 
+// C = L^T R for 64 x 64 blocks over 64 reduction rows, C[i][j] =
+// sum_e L[e][i] R[e][j] (L, R row-major with pitches ll, lr), on the
+// 16 x 16 x 4 float64 MFMA: 2 x 2 wavefronts of 32 x 32, each lane loading
+// its own operands from memory (lane l: row 4 s + l / 16, column l % 16 of
+// a 16-wide column strip, 16 consecutive doubles per 16 lanes).  All loads
+// of a wavefront are issued before its first MFMA.
+__device__ __forceinline__ void block_tn(const double* Lp, int64_t ll, const double* Rp, int64_t lr,
+                                         f64x4 (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int ci = (wave >> 1) * 32 + (lane & 15), cj = (wave & 1) * 32 + (lane & 15);
+  gptr<const double> L = to_global(Lp);
+  gptr<const double> R = to_global(Rp);
+  double a[NB / 4][2], b[NB / 4][2];
+#pragma unroll
+  for (int s = 0; s < NB / 4; ++s)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      a[s][f] = L[(4 * s + g) * ll + ci + 16 * f];
+      b[s][f] = R[(4 * s + g) * lr + cj + 16 * f];
+    }
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < NB / 4; ++s)
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s][fm], b[s][fn], acc[fm][fn], 0, 0, 0);
+}
+
+// Offset of the element lane holds in register v of output block (fm, fn)
+// of block_tn (16 x 16 float64 MFMA output: row l / 16 + 4 v, column l % 16).
+__device__ __forceinline__ int64_t block_off(int fm, int fn, int v, int64_t ld) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = (wave >> 1) * 32 + fm * 16 + (lane >> 4) + 4 * v;
+  const int col = (wave & 1) * 32 + fn * 16 + (lane & 15);
+  return row * ld + col;
+}
+
 __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
   MatDesc d;
   ClassInfo ci;
@@ -81,6 +124,7 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
 __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
   __shared__ double a[NB][LP];
   __shared__ double z[NB][LP];
+  __shared__ double sd[NB];
   __shared__ int bad;
   MatDesc d;
   ClassInfo ci;
@@ -95,13 +139,14 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
   const double* Sd = Dinv + NB * NB + o;
   load_block(a, A + o * rp + o, rp);
   for (int e = threadIdx.x; e < NB * NB; e += kThreads) z[e / NB][e % NB] = (e / NB == e % NB) ? 1.0 : 0.0;
+  if (threadIdx.x < NB) sd[threadIdx.x] = Sd[threadIdx.x];
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
   const int tid = threadIdx.x;
   for (int k = 0; k < NB; ++k) {
     if (tid < NB) {   // wavefront 0: pivot and row k of T and of Y
       const double dk = a[k][k];
-      const bool ok = dk > kPivotTol * Sd[k] && dk < INFINITY;
+      const bool ok = dk > kPivotTol * sd[k] && dk < INFINITY;
       const double t = sqrt(dk), inv = 1.0 / t;
       if (!ok && tid == 0) bad = 1;
       if (tid > k) a[k][tid] *= inv;
@@ -132,8 +177,6 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
 
 // out = Dinv^T * in for one 64 x 64 block, in place.
 __global__ __launch_bounds__(kThreads) void k_chol_panel(Launch L) {
-  __shared__ double dl[NB][LP];
-  __shared__ double in[NB][LP];
   MatDesc d;
   ClassInfo ci;
   int local;
@@ -144,34 +187,20 @@ __global__ __launch_bounds__(kThreads) void k_chol_panel(Launch L) {
   const int right = nblk - kb - 1;
   double* blk = local < right ? dptr(L, d.oA) + o * rp + (kb + 1 + local) * NB
                               : dptr(L, d.oY) + o * rp + (local - right) * NB;
-  load_block(dl, dptr(L, d.oD), NB);
-  load_block(in, blk, rp);
-  __syncthreads();
-  const int ta = threadIdx.x / 16, tb = threadIdx.x % 16;
-  double acc[4][4] = {};
-  const int emax = 4 * ta + 3;   // Dinv[e][a] = 0 for e > a
-  for (int e = 0; e <= emax; ++e) {
-    double x[4], y[4];
+  f64x4 acc[2][2];
+  block_tn(dptr(L, d.oD), NB, blk, rp, acc);
+  __syncthreads();   // every wavefront has read the block before any writes it
+  gptr<double> out = to_global(blk);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      x[u] = dl[e][4 * ta + u];
-      y[u] = in[e][4 * tb + u];
-    }
+  for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) acc[u][w] += x[u] * y[w];
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) blk[(4 * ta + u) * rp + 4 * tb + w] = acc[u][w];
+      for (int v = 0; v < 4; ++v) out[block_off(fm, fn, v, rp)] = acc[fm][fn][v];
 }
 
 // Trailing update of the factorization and of the identity block columns.
 __global__ __launch_bounds__(kThreads) void k_chol_trail(Launch L) {
-  __shared__ double lt[NB][LP];
-  __shared__ double rt[NB][LP];
   MatDesc d;
   ClassInfo ci;
   int local;
@@ -205,30 +234,18 @@ __global__ __launch_bounds__(kThreads) void k_chol_trail(Launch L) {
     out = Y + static_cast<int64_t>(bi) * NB * rp + c * NB;
     assign = c == kb;   // first write of this block of Y
   }
-  load_block(lt, left, rp);
-  load_block(rt, rgt, rp);
-  __syncthreads();
-  const int ta = threadIdx.x / 16, tb = threadIdx.x % 16;
-  double acc[4][4] = {};
-  for (int e = 0; e < NB; ++e) {
-    double x[4], y[4];
+  f64x4 acc[2][2];
+  block_tn(left, rp, rgt, rp, acc);
+  gptr<double> q = to_global(out);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      x[u] = lt[e][4 * ta + u];
-      y[u] = rt[e][4 * tb + u];
-    }
+  for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) acc[u][w] += x[u] * y[w];
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      double* q = out + (4 * ta + u) * rp + 4 * tb + w;
-      *q = assign ? -acc[u][w] : *q - acc[u][w];
-    }
+      for (int v = 0; v < 4; ++v) {
+        const int64_t e = block_off(fm, fn, v, rp);
+        q[e] = assign ? -acc[fm][fn][v] : q[e] - acc[fm][fn][v];
+      }
 }
 
 template <class K>
