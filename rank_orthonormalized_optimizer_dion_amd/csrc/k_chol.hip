@@ -21,7 +21,6 @@ namespace dion {
 namespace {
 
 constexpr int NB = kCholNB;
-constexpr int LP = NB + 1;   // LDS row pitch (doubles)
 
 // A pivot below this fraction of the column's original squared norm means
 // the factor's condition number is beyond about 1e3, where the float32
@@ -35,16 +34,6 @@ __device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
 
 __device__ __forceinline__ double* dptr(const Launch& L, int64_t off) {
   return reinterpret_cast<double*>(L.ws + off);
-}
-
-// Load a 64 x 64 block at src (row pitch ld doubles) into LDS.
-__device__ __forceinline__ void load_block(double (*dst)[LP], const double* src, int64_t ld) {
-  for (int e = threadIdx.x; e < NB * NB / 2; e += kThreads) {
-    const int i = e / (NB / 2), j2 = e % (NB / 2);
-    const double2 v = *reinterpret_cast<const double2*>(src + i * ld + 2 * j2);
-    dst[i][2 * j2] = v.x;
-    dst[i][2 * j2 + 1] = v.y;
-  }
 }
 
 // C = L^T R for 64 x 64 blocks over 64 reduction rows, C[i][j] =
@@ -121,11 +110,19 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
   }
 }
 
+// One 64 x 64 diagonal block: T_kk (upper, positive diagonal) with
+// T_kk^T T_kk = A_kk, and Z = T_kk^{-T} from the same row operations on an
+// identity block.  Thread (wavefront w, lane c) keeps rows 4 q + w of column
+// c of both in registers; step k's scaled pivot row is broadcast through a
+// double-buffered LDS row, so one barrier per step suffices (a buffer is
+// rewritten two steps later, after every thread has passed the barrier that
+// follows its last read).  A failed pivot is flagged in the same buffer, so
+// every wavefront leaves the loop at the same step.
 __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
-  __shared__ double a[NB][LP];
-  __shared__ double z[NB][LP];
+  __shared__ double rowA[2][NB];
+  __shared__ double rowZ[2][NB];
   __shared__ double sd[NB];
-  __shared__ int bad;
+  __shared__ int badf[2];
   MatDesc d;
   ClassInfo ci;
   int local;
@@ -133,45 +130,59 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
   if (skipped(L, d)) return;
   const int kb = L.kb;
   const int64_t rp = d.rp, o = static_cast<int64_t>(kb) * NB;
-  double* A = dptr(L, d.oA);
-  double* Y = dptr(L, d.oY);
-  double* Dinv = dptr(L, d.oD);
-  const double* Sd = Dinv + NB * NB + o;
-  load_block(a, A + o * rp + o, rp);
-  for (int e = threadIdx.x; e < NB * NB; e += kThreads) z[e / NB][e % NB] = (e / NB == e % NB) ? 1.0 : 0.0;
-  if (threadIdx.x < NB) sd[threadIdx.x] = Sd[threadIdx.x];
-  if (threadIdx.x == 0) bad = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  gptr<const double> A = to_global(dptr(L, d.oA) + o * rp + o);
+  double a[NB / 4], z[NB / 4];
+#pragma unroll
+  for (int q = 0; q < NB / 4; ++q) {
+    a[q] = A[(4 * q + wave) * rp + lane];
+    z[q] = 4 * q + wave == lane ? 1.0 : 0.0;
+  }
+  if (threadIdx.x < NB) sd[threadIdx.x] = dptr(L, d.oD)[NB * NB + o + threadIdx.x];
   __syncthreads();
-  const int tid = threadIdx.x;
-  for (int k = 0; k < NB; ++k) {
-    if (tid < NB) {   // wavefront 0: pivot and row k of T and of Y
-      const double dk = a[k][k];
-      const bool ok = dk > kPivotTol * sd[k] && dk < INFINITY;
-      const double t = sqrt(dk), inv = 1.0 / t;
-      if (!ok && tid == 0) bad = 1;
-      if (tid > k) a[k][tid] *= inv;
-      else if (tid == k) a[k][k] = t;
-      if (tid <= k) z[k][tid] *= inv;
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < NB / 4; ++q) {
+    for (int w = 0; w < 4; ++w) {
+      const int k = 4 * q + w, buf = k & 1;
+      if (wave == w) {   // this wavefront holds row k
+        const double dk = __shfl(a[q], k, 64);
+        const bool ok = dk > kPivotTol * sd[k] && dk < INFINITY;
+        const double t = sqrt(dk), inv = 1.0 / t;
+        a[q] = lane > k ? a[q] * inv : (lane == k ? t : 0.0);
+        z[q] = lane <= k ? z[q] * inv : 0.0;
+        rowA[buf][lane] = a[q];
+        rowZ[buf][lane] = z[q];
+        if (lane == 0) badf[buf] = ok ? 0 : 1;
+      }
+      __syncthreads();
+      if (badf[buf]) {
+        bad = true;
+        break;
+      }
+      const double rj = rowA[buf][lane], zj = rowZ[buf][lane];
+#pragma unroll
+      for (int qq = q; qq < NB / 4; ++qq) {
+        if (qq == q && wave <= w) continue;   // rows 4 qq + wave <= k
+        const double ai = rowA[buf][4 * qq + wave];
+        if (lane > k) a[qq] -= ai * rj;
+        z[qq] -= ai * zj;
+      }
     }
-    __syncthreads();
     if (bad) break;
-    for (int e = tid; e < NB * NB; e += kThreads) {
-      const int i = e / NB, j = e % NB;
-      if (i <= k) continue;
-      if (j >= i) a[i][j] -= a[k][i] * a[k][j];
-      else if (j <= k) z[i][j] -= a[k][i] * z[k][j];
-    }
-    __syncthreads();
   }
   if (bad) {
-    if (tid == 0) atomicOr(&L.status[d.slot], L.flag);
+    if (threadIdx.x == 0) atomicOr(&L.status[d.slot], L.flag);
     return;
   }
-  // Dinv = T_kk^{-1} = z^T (upper), Y_kk = z (lower, zeros above).
-  for (int e = tid; e < NB * NB; e += kThreads) {
-    const int i = e / NB, j = e % NB;
-    Dinv[e] = i <= j ? z[j][i] : 0.0;
-    Y[(o + i) * rp + o + j] = z[i][j];
+  // Dinv = T_kk^{-1} = Z^T (upper triangular), Y_kk = Z (lower, zeros above).
+  gptr<double> Dinv = to_global(dptr(L, d.oD));
+  gptr<double> Y = to_global(dptr(L, d.oY) + o * rp + o);
+#pragma unroll
+  for (int q = 0; q < NB / 4; ++q) {
+    const int i = 4 * q + wave;
+    Dinv[lane * NB + i] = lane <= i ? z[q] : 0.0;
+    Y[i * rp + lane] = z[q];
   }
 }
 
