@@ -247,6 +247,56 @@ __device__ __forceinline__ void bf_store_quad(u32x2* hi, u32x2* lo, int kq, int 
   lo[slot] = l;
 }
 
+// Loader of split-bfloat16 planes written ahead of time (hi and lo, row
+// pitch `pitch` cells of 8 bfloat16, zero past the reduction length): cell
+// (x, k8) of the tile is one 16-byte load per plane and one 16-byte LDS store
+// per plane, in the BfShape layout.  The reduction range is whole tiles;
+// FULL: every row x of the tile exists.
+template <int BX, int BK>
+struct LoadPl {
+  static constexpr int K8 = BK / 8;
+  static constexpr int NV = BX * K8 / kThreads;
+  static_assert(NV >= 1 && BX * K8 % kThreads == 0, "tile too small");
+  gptr<const u32x4> hi, lo;
+  int64_t pitch;
+  int x0, xmax;
+  u32x4 vh[NV], vl[NV];
+
+  __device__ __forceinline__ LoadPl(const void* h, const void* l, int64_t pitch_, int x0_, int xmax_)
+      : hi(to_global(static_cast<const u32x4*>(h))), lo(to_global(static_cast<const u32x4*>(l))),
+        pitch(pitch_), x0(x0_), xmax(xmax_) {}
+
+  template <bool FULL>
+  __device__ __forceinline__ void load(int k0) {
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      const int k8 = idx % K8, x = idx / K8;
+      const int64_t o = static_cast<int64_t>(x0 + x) * pitch + k0 / 8 + k8;
+      if (FULL || x0 + x < xmax) {
+        vh[s] = hi[o];
+        vl[s] = lo[o];
+      } else {
+        vh[s] = u32x4{0u, 0u, 0u, 0u};
+        vl[s] = vh[s];
+      }
+    }
+  }
+  __device__ __forceinline__ void store(u32x4* sh, u32x4* sl) const {
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      const int k8 = idx % K8, x = idx / K8;
+      const int c = k8 * BfShape<BX, BK>::PITCH + bf_swz(x);
+      sh[c] = vh[s];
+      sl[c] = vl[s];
+    }
+  }
+  __device__ __forceinline__ void store_bf(u32x2* hi, u32x2* lo) const {
+    store(reinterpret_cast<u32x4*>(hi), reinterpret_cast<u32x4*>(lo));
+  }
+};
+
 // Loader for a source whose reduction index is contiguous:
 // element (x, k) = src[x * ld + k].  Each row of the tile is read as BK/4
 // consecutive float4 (full 128-byte lines for BK = 32).

@@ -206,7 +206,8 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     d.r = k.r;
     d.rp = k.rp;
     d.slot = i;
-    const size_t m = k.m, n = k.n, r = k.r, rp = k.rp;
+    d.kp = cdiv(k.m, kPlaneK) * kPlaneK;
+    const size_t m = k.m, n = k.n, r = k.r, rp = k.rp, kp = d.kp;
     auto take = [&](size_t bytes) {
       const size_t o = off;
       off = align_up(off + bytes);
@@ -222,6 +223,7 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     d.oN = take(r * 4);
     const size_t kpart = std::max(k.s_mv > 1 ? k.s_mv * m * r : 0, k.s_mtu > 1 ? k.s_mtu * n * r : 0);
     d.oK = kpart ? take(kpart * 4) : 0;
+    d.oH = p.math ? take(r * kp * 4) : 0;
     p.table[g] = d;
   }
   p.ws_bytes = off;
@@ -360,7 +362,16 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   DION_TRY(orth(p, base, 0, st));
   DION_TRY(mk.mark(2, st));
 
-  // W = M^T U
+  // W = M^T U (split-bfloat16: U^T split once into planes, read as whole
+  // cells by every tile)
+  if (p.math) {
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      ci.tx = cdiv(c.m, kSplitTile);
+      ci.ty = cdiv(c.r, kSplitTile);
+      ci.tiles = ci.tx * ci.ty;
+      return true;
+    }, [&](const Launch& L) { return launch_split_t(L, st); }));
+  }
   for (int bn : {128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_r != bn) return false;

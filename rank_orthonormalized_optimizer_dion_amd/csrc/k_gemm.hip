@@ -357,8 +357,10 @@ __device__ __forceinline__ void mtu3_body(const Launch& L, const MatDesc& d, con
   constexpr int BK = 32;
   const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
   LoadXC<BM, BK, VEC, SrcM<GT>> la0(sm, d.n, tm * BM, d.n, kend), la1 = la0;
-  const float* U = reinterpret_cast<const float*>(L.ws + d.oB);
-  LoadXC<BN, BK, VEC, SrcF32> lb0(SrcF32{U}, d.r, tn * BN, d.r, kend), lb1 = lb0;
+  // U^T planes (r x kp, zero past column m): cells of 8 consecutive rows of U
+  static_assert(kPlaneK % BK == 0, "planes hold whole reduction tiles");
+  const uint16_t* ut = reinterpret_cast<const uint16_t*>(L.ws + d.oH);
+  LoadPl<BN, BK> lb0(ut, ut + static_cast<int64_t>(d.r) * d.kp, d.kp / 8, tn * BN, d.r), lb1 = lb0;
   f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
   zero_acc(acc);
   pipeline2_bf<BM, BN, BK, FULL>(

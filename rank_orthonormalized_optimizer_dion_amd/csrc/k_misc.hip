@@ -2,6 +2,7 @@
 //   k_reduce    sum of split-K partial products, in a fixed order
 //   k_colnorm   Dion's rule, part 1: inverse Euclidean norms of W's columns
 //   k_colscale  Dion's rule, part 2: Vbar = W diag(1/||w_j||) written into V
+//   k_split_t   split-bfloat16 planes of U^T for M^T U
 // (right-factor rule of the Orth-Dion page's closing remark; column scaling
 // as the Orth-Dion abstract describes it).
 #include <math.h>
@@ -91,6 +92,64 @@ __global__ __launch_bounds__(kThreads) void k_colscale(Launch L) {
   }
 }
 
+// U^T (r x m, from U: m x r float32) as hi / lo bfloat16 planes of row
+// pitch kp (zero in columns m .. kp), split as BfShape describes, so that
+// M^T U reads its U operand as whole 16-byte cells of 8 consecutive rows of
+// U.  One workgroup per 64 x 64 tile of U: coalesced float4 row reads into
+// LDS, then each thread splits two cells (8 rows of one column each).
+__global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
+  constexpr int T = kSplitTile;
+  __shared__ float tile[T][T + 1];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int ti = local / ci.ty, tj = local % ci.ty;
+  const int i0 = ti * T, j0 = tj * T;
+  gptr<const float> U = to_global(reinterpret_cast<const float*>(L.ws + d.oB));
+  const bool vec = (d.r & 3) == 0;
+#pragma unroll
+  for (int s = 0; s < T * T / 4 / kThreads; ++s) {
+    const int e = threadIdx.x + kThreads * s;
+    const int i = e / (T / 4), j = 4 * (e % (T / 4));
+    const int gi = i0 + i, gj = j0 + j;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (gi < d.m) {
+      const int64_t o = static_cast<int64_t>(gi) * d.r + gj;
+      if (vec && gj + 3 < d.r) {
+        v = *(gptr<const f32x4>)(U + o);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = gj + c < d.r ? U[o + c] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) tile[i][j + c] = v[c];
+  }
+  __syncthreads();
+  uint16_t* hi = reinterpret_cast<uint16_t*>(L.ws + d.oH);
+  const int64_t plane = static_cast<int64_t>(d.r) * d.kp;
+#pragma unroll
+  for (int s = 0; s < T * T / 8 / kThreads; ++s) {
+    const int c = threadIdx.x + kThreads * s;
+    const int j = c / (T / 8), i = 8 * (c % (T / 8));
+    if (j0 + j >= d.r || i0 + i >= d.kp) continue;
+    f32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = tile[i + e][j];
+      b[e] = tile[i + 4 + e][j];
+    }
+    u32x2 ha, la, hb, lb;
+    bf_split4(a, ha, la);
+    bf_split4(b, hb, lb);
+    const int64_t o = static_cast<int64_t>(j0 + j) * d.kp + i0 + i;
+    *(gptr<u32x4>)(to_global(hi) + o) = u32x4{ha.x, ha.y, hb.x, hb.y};
+    *(gptr<u32x4>)(to_global(hi) + plane + o) = u32x4{la.x, la.y, lb.x, lb.y};
+  }
+}
+
 template <class K>
 hipError_t go(K kernel, const Launch& L, hipStream_t st) {
   if (L.total <= 0) return hipSuccess;
@@ -104,5 +163,6 @@ int elems_per_tile() { return kElemsPerTile; }
 hipError_t launch_reduce(const Launch& L, hipStream_t st) { return go(k_reduce, L, st); }
 hipError_t launch_colnorm(const Launch& L, hipStream_t st) { return go(k_colnorm, L, st); }
 hipError_t launch_colscale(const Launch& L, hipStream_t st) { return go(k_colscale, L, st); }
+hipError_t launch_split_t(const Launch& L, hipStream_t st) { return go(k_split_t, L, st); }
 
 }  // namespace dion
