@@ -247,24 +247,33 @@ __device__ __forceinline__ void bf_store_quad(u32x2* hi, u32x2* lo, int kq, int 
   lo[slot] = l;
 }
 
-// Loader of split-bfloat16 planes written ahead of time (hi and lo, row
-// pitch `pitch` cells of 8 bfloat16, zero past the reduction length): cell
-// (x, k8) of the tile is one 16-byte load per plane and one 16-byte LDS store
-// per plane, in the BfShape layout.  The reduction range is whole tiles;
-// FULL: every row x of the tile exists.
+// Cell (x, k8) (16 bytes: elements k = 8 k8 .. 8 k8 + 7 of row x) of a
+// split-bfloat16 plane with `rows` rows, K-blocked by kPlaneK: the cells of
+// one kPlaneK slice of all rows are contiguous, row after row.
+__device__ __forceinline__ int64_t plane_cell(int64_t rows, int x, int k8) {
+  constexpr int CB = kPlaneK / 8;
+  return ((k8 / CB) * rows + x) * CB + k8 % CB;
+}
+
+// Loader of split-bfloat16 planes written ahead of time (hi and lo, zero
+// past the reduction length) in the K-blocked cell order of plane_cell():
+// the BK = kPlaneK slice of BX consecutive rows is one contiguous run of
+// 16-byte cells, read with one 16-byte load per cell and plane and stored
+// to LDS in the BfShape layout.  FULL: every row x of the tile exists.
 template <int BX, int BK>
 struct LoadPl {
+  static_assert(BK == kPlaneK, "one plane block per reduction tile");
   static constexpr int K8 = BK / 8;
   static constexpr int NV = BX * K8 / kThreads;
   static_assert(NV >= 1 && BX * K8 % kThreads == 0, "tile too small");
   gptr<const u32x4> hi, lo;
-  int64_t pitch;
+  int64_t rows;
   int x0, xmax;
   u32x4 vh[NV], vl[NV];
 
-  __device__ __forceinline__ LoadPl(const void* h, const void* l, int64_t pitch_, int x0_, int xmax_)
+  __device__ __forceinline__ LoadPl(const void* h, const void* l, int64_t rows_, int x0_, int xmax_)
       : hi(to_global(static_cast<const u32x4*>(h))), lo(to_global(static_cast<const u32x4*>(l))),
-        pitch(pitch_), x0(x0_), xmax(xmax_) {}
+        rows(rows_), x0(x0_), xmax(xmax_) {}
 
   template <bool FULL>
   __device__ __forceinline__ void load(int k0) {
@@ -272,7 +281,7 @@ struct LoadPl {
     for (int s = 0; s < NV; ++s) {
       const int idx = threadIdx.x + kThreads * s;
       const int k8 = idx % K8, x = idx / K8;
-      const int64_t o = static_cast<int64_t>(x0 + x) * pitch + k0 / 8 + k8;
+      const int64_t o = plane_cell(rows, x0 + x, k0 / 8 + k8);
       if (FULL || x0 + x < xmax) {
         vh[s] = hi[o];
         vl[s] = lo[o];

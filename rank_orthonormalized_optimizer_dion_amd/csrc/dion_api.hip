@@ -206,8 +206,7 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     d.r = k.r;
     d.rp = k.rp;
     d.slot = i;
-    d.kp = cdiv(k.m, kPlaneK) * kPlaneK;
-    const size_t m = k.m, n = k.n, r = k.r, rp = k.rp, kp = d.kp;
+    const size_t m = k.m, n = k.n, r = k.r, rp = k.rp;
     auto take = [&](size_t bytes) {
       const size_t o = off;
       off = align_up(off + bytes);
@@ -223,7 +222,7 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     d.oN = take(r * 4);
     const size_t kpart = std::max(k.s_mv > 1 ? k.s_mv * m * r : 0, k.s_mtu > 1 ? k.s_mtu * n * r : 0);
     d.oK = kpart ? take(kpart * 4) : 0;
-    d.oH = p.math ? take(r * kp * 4) : 0;
+    d.oH = p.math ? take(r * std::max(plane_pitch(k.m), plane_pitch(k.n)) * 4) : 0;
     p.table[g] = d;
   }
   p.ws_bytes = off;
@@ -317,6 +316,17 @@ hipError_t orth(const dion_plan& p, Launch base, int which, hipStream_t st) {
   return hipSuccess;
 }
 
+// Split-bfloat16 planes of V^T (which = 0) or U^T (which = 1).
+hipError_t split_t(const dion_plan& p, Launch base, int which, hipStream_t st) {
+  base.which = which;
+  return grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+    ci.tx = cdiv(which == 0 ? c.n : c.m, kSplitTile);
+    ci.ty = cdiv(c.r, kSplitTile);
+    ci.tiles = ci.tx * ci.ty;
+    return true;
+  }, [&](const Launch& L) { return launch_split_t(L, st); });
+}
+
 // Records the phase-boundary event `b` of the current timed step, if any.
 struct Marker {
   hipEvent_t* ev = nullptr;
@@ -336,8 +346,10 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   base.beta = beta;
   const int ept = elems_per_tile();
 
-  // P = M V
+  // P = M V (split-bfloat16: V^T split once into planes, read as whole cells
+  // by every tile)
   DION_TRY(mk.mark(0, st));
+  if (p.math) DION_TRY(split_t(p, base, 0, st));
   for (int bn : {128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_r != bn) return false;
@@ -364,14 +376,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
 
   // W = M^T U (split-bfloat16: U^T split once into planes, read as whole
   // cells by every tile)
-  if (p.math) {
-    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-      ci.tx = cdiv(c.m, kSplitTile);
-      ci.ty = cdiv(c.r, kSplitTile);
-      ci.tiles = ci.tx * ci.ty;
-      return true;
-    }, [&](const Launch& L) { return launch_split_t(L, st); }));
-  }
+  if (p.math) DION_TRY(split_t(p, base, 1, st));
   for (int bn : {128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_r != bn) return false;

@@ -9,6 +9,7 @@ constexpr int kCholNB = 64;
 // Split-bfloat16 planes of a factor are padded to a multiple of this many
 // columns (the reduction tile of the kernels that read them).
 constexpr int kPlaneK = 32;
+inline __host__ __device__ int plane_pitch(int rows) { return (rows + kPlaneK - 1) / kPlaneK * kPlaneK; }
 // Grouped launches carry at most this many shape classes.
 constexpr int kMaxClasses = 8;
 
@@ -21,7 +22,7 @@ struct MatDesc {
   float* V;
   int32_t m, n, r, rp;
   int32_t slot;      // index in the caller's list = status word index
-  int32_t kp;        // m rounded up to kPlaneK: row pitch of the U^T planes
+  int32_t pad0;
   int64_t oP;        // m x r      float32: P = M V, then U
   int64_t oB;        // max(m,n) x r float32: first CholeskyQR pass output
   int64_t oW;        // n x r      float32: W = M^T U
@@ -31,8 +32,9 @@ struct MatDesc {
   int64_t oD;        // kCholNB^2 + rp float64: diagonal-block inverse, diag(S)
   int64_t oN;        // r          float32: inverse column norms (Dion)
   int64_t oK;        // split-K partial products (float32)
-  int64_t oH;        // r x kp bfloat16 x 2: split-bfloat16 planes of U^T
-                     // (hi, then lo; zero past column m); 0 without them
+  int64_t oH;        // split-bfloat16 planes (hi, then lo) of V^T during
+                     // M V, of U^T during M^T U: r x plane_pitch(rows)
+                     // bfloat16 each, zero past the last row; 0 without them
 };
 
 // Matrices with the same (m, n, r) form a class; inside one launch every

@@ -317,7 +317,11 @@ __device__ __forceinline__ void mv3_body(const Launch& L, const MatDesc& d, cons
   constexpr int BK = 32;
   const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
   LoadKC<BM, BK, VEC, false, SrcM<GT>> la0(sm, d.n, tm * BM, d.m, kend), la1 = la0;
-  LoadXC<BN, BK, VEC, SrcF32> lb0(SrcF32{d.V}, d.r, tn * BN, d.r, kend), lb1 = lb0;
+  // V^T planes (r rows of plane_pitch(n), zero past column n): cells of 8
+  // consecutive rows of V
+  const uint16_t* vt = reinterpret_cast<const uint16_t*>(L.ws + d.oH);
+  LoadPl<BN, BK> lb0(vt, vt + static_cast<int64_t>(d.r) * plane_pitch(d.n), d.r, tn * BN, d.r),
+      lb1 = lb0;
   f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
   zero_acc(acc);
   pipeline2_bf<BM, BN, BK, FULL>(
@@ -332,7 +336,7 @@ __device__ __forceinline__ void mv3_body(const Launch& L, const MatDesc& d, cons
 }
 
 template <typename GT, int BN, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_mv3(Launch L) {
+__global__ __launch_bounds__(kThreads, 2) void k_mv3(Launch L) {
   constexpr int BK = 32;
   __shared__ u32x4 smem[2 * bf_stage_cells<BM, BN, BK>()];
   MatDesc d;
@@ -357,10 +361,11 @@ __device__ __forceinline__ void mtu3_body(const Launch& L, const MatDesc& d, con
   constexpr int BK = 32;
   const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
   LoadXC<BM, BK, VEC, SrcM<GT>> la0(sm, d.n, tm * BM, d.n, kend), la1 = la0;
-  // U^T planes (r x kp, zero past column m): cells of 8 consecutive rows of U
-  static_assert(kPlaneK % BK == 0, "planes hold whole reduction tiles");
+  // U^T planes (r rows of plane_pitch(m), zero past column m): cells of 8
+  // consecutive rows of U
   const uint16_t* ut = reinterpret_cast<const uint16_t*>(L.ws + d.oH);
-  LoadPl<BN, BK> lb0(ut, ut + static_cast<int64_t>(d.r) * d.kp, d.kp / 8, tn * BN, d.r), lb1 = lb0;
+  LoadPl<BN, BK> lb0(ut, ut + static_cast<int64_t>(d.r) * plane_pitch(d.m), d.r, tn * BN, d.r),
+      lb1 = lb0;
   f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
   zero_acc(acc);
   pipeline2_bf<BM, BN, BK, FULL>(
@@ -375,7 +380,7 @@ __device__ __forceinline__ void mtu3_body(const Launch& L, const MatDesc& d, con
 }
 
 template <typename GT, int BN, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_mtu3(Launch L) {
+__global__ __launch_bounds__(kThreads, 2) void k_mtu3(Launch L) {
   constexpr int BK = 32;
   __shared__ u32x4 smem[2 * bf_stage_cells<BM, BN, BK>()];
   MatDesc d;

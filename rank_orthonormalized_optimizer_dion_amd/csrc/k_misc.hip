@@ -2,7 +2,7 @@
 //   k_reduce    sum of split-K partial products, in a fixed order
 //   k_colnorm   Dion's rule, part 1: inverse Euclidean norms of W's columns
 //   k_colscale  Dion's rule, part 2: Vbar = W diag(1/||w_j||) written into V
-//   k_split_t   split-bfloat16 planes of U^T for M^T U
+//   k_split_t   split-bfloat16 planes of V^T for M V, of U^T for M^T U
 // (right-factor rule of the Orth-Dion page's closing remark; column scaling
 // as the Orth-Dion abstract describes it).
 #include <math.h>
@@ -92,11 +92,12 @@ __global__ __launch_bounds__(kThreads) void k_colscale(Launch L) {
   }
 }
 
-// U^T (r x m, from U: m x r float32) as hi / lo bfloat16 planes of row
-// pitch kp (zero in columns m .. kp), split as BfShape describes, so that
-// M^T U reads its U operand as whole 16-byte cells of 8 consecutive rows of
-// U.  One workgroup per 64 x 64 tile of U: coalesced float4 row reads into
-// LDS, then each thread splits two cells (8 rows of one column each).
+// Q^T (r x rows, from Q: rows x r float32; Q = V for which = 0, U for
+// which = 1) as hi / lo bfloat16 planes of row pitch plane_pitch(rows)
+// (zero past column rows) in the K-blocked cell order of plane_cell(),
+// split as BfShape describes, so that M V and M^T U read their rank-r
+// operand as contiguous runs of 16-byte cells of 8 consecutive rows of Q.  One workgroup per 64 x 64 tile of Q: coalesced float4 row
+// reads into LDS, then each thread splits two cells (8 rows of one column).
 __global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
   constexpr int T = kSplitTile;
   __shared__ float tile[T][T + 1];
@@ -104,10 +105,13 @@ __global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
   ClassInfo ci;
   int local;
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
-  if (skipped(L, d)) return;
+  // The V split opens the step, before M V clears the status words: a
+  // breakdown flagged by the previous step must not skip it.
+  if (L.which == 1 && skipped(L, d)) return;
   const int ti = local / ci.ty, tj = local % ci.ty;
   const int i0 = ti * T, j0 = tj * T;
-  gptr<const float> U = to_global(reinterpret_cast<const float*>(L.ws + d.oB));
+  const int rows = L.which == 0 ? d.n : d.m, kp = plane_pitch(rows);
+  gptr<const float> Q = to_global(L.which == 0 ? d.V : reinterpret_cast<const float*>(L.ws + d.oB));
   const bool vec = (d.r & 3) == 0;
 #pragma unroll
   for (int s = 0; s < T * T / 4 / kThreads; ++s) {
@@ -115,13 +119,13 @@ __global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
     const int i = e / (T / 4), j = 4 * (e % (T / 4));
     const int gi = i0 + i, gj = j0 + j;
     f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (gi < d.m) {
+    if (gi < rows) {
       const int64_t o = static_cast<int64_t>(gi) * d.r + gj;
       if (vec && gj + 3 < d.r) {
-        v = *(gptr<const f32x4>)(U + o);
+        v = *(gptr<const f32x4>)(Q + o);
       } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = gj + c < d.r ? U[o + c] : 0.0f;
+        for (int c = 0; c < 4; ++c) v[c] = gj + c < d.r ? Q[o + c] : 0.0f;
       }
     }
 #pragma unroll
@@ -129,12 +133,12 @@ __global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
   }
   __syncthreads();
   uint16_t* hi = reinterpret_cast<uint16_t*>(L.ws + d.oH);
-  const int64_t plane = static_cast<int64_t>(d.r) * d.kp;
+  const int64_t plane = static_cast<int64_t>(d.r) * kp;
 #pragma unroll
   for (int s = 0; s < T * T / 8 / kThreads; ++s) {
     const int c = threadIdx.x + kThreads * s;
     const int j = c / (T / 8), i = 8 * (c % (T / 8));
-    if (j0 + j >= d.r || i0 + i >= d.kp) continue;
+    if (j0 + j >= d.r || i0 + i >= kp) continue;
     f32x4 a, b;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -144,9 +148,10 @@ __global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
     u32x2 ha, la, hb, lb;
     bf_split4(a, ha, la);
     bf_split4(b, hb, lb);
-    const int64_t o = static_cast<int64_t>(j0 + j) * d.kp + i0 + i;
-    *(gptr<u32x4>)(to_global(hi) + o) = u32x4{ha.x, ha.y, hb.x, hb.y};
-    *(gptr<u32x4>)(to_global(hi) + plane + o) = u32x4{la.x, la.y, lb.x, lb.y};
+    const int64_t o = plane_cell(d.r, j0 + j, (i0 + i) / 8);
+    gptr<u32x4> ph = (gptr<u32x4>)to_global(hi);
+    ph[o] = u32x4{ha.x, ha.y, hb.x, hb.y};
+    ph[plane / 8 + o] = u32x4{la.x, la.y, lb.x, lb.y};
   }
 }
 

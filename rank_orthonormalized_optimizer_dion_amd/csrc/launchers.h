@@ -23,7 +23,8 @@ hipError_t launch_chol_trail(const Launch& L, hipStream_t st);
 hipError_t launch_reduce(const Launch& L, hipStream_t st);
 hipError_t launch_colnorm(const Launch& L, hipStream_t st);
 hipError_t launch_colscale(const Launch& L, hipStream_t st);
-// U^T split-bfloat16 planes, in kSplitTile x kSplitTile tiles of U
+// V^T (which = 0) or U^T (which = 1) split-bfloat16 planes, in
+// kSplitTile x kSplitTile tiles of V or U
 constexpr int kSplitTile = 64;
 hipError_t launch_split_t(const Launch& L, hipStream_t st);
 int elems_per_tile();
