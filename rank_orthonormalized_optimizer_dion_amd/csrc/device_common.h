@@ -260,12 +260,12 @@ __device__ __forceinline__ int64_t plane_cell(int64_t rows, int x, int k8) {
 // the BK = kPlaneK slice of BX consecutive rows is one contiguous run of
 // 16-byte cells, read with one 16-byte load per cell and plane and stored
 // to LDS in the BfShape layout.  FULL: every row x of the tile exists.
-template <int BX, int BK>
+template <int BX, int BK, int NT = kThreads>
 struct LoadPl {
   static_assert(BK == kPlaneK, "one plane block per reduction tile");
   static constexpr int K8 = BK / 8;
-  static constexpr int NV = BX * K8 / kThreads;
-  static_assert(NV >= 1 && BX * K8 % kThreads == 0, "tile too small");
+  static constexpr int NV = BX * K8 / NT;
+  static_assert(NV >= 1 && BX * K8 % NT == 0, "tile too small");
   gptr<const u32x4> hi, lo;
   int64_t rows;
   int x0, xmax;
@@ -279,7 +279,7 @@ struct LoadPl {
   __device__ __forceinline__ void load(int k0) {
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       const int k8 = idx % K8, x = idx / K8;
       const int64_t o = plane_cell(rows, x0 + x, k0 / 8 + k8);
       if (FULL || x0 + x < xmax) {
@@ -294,7 +294,7 @@ struct LoadPl {
   __device__ __forceinline__ void store(u32x4* sh, u32x4* sl) const {
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       const int k8 = idx % K8, x = idx / K8;
       const int c = k8 * BfShape<BX, BK>::PITCH + bf_swz(x);
       sh[c] = vh[s];
@@ -313,11 +313,11 @@ struct LoadPl {
 // triangle).
 // FULL (load): the whole tile lies inside the operand, so loads are
 // unconditional; otherwise every element is bounds-checked.
-template <int BX, int BK, bool VEC, bool TRI, class Src>
+template <int BX, int BK, bool VEC, bool TRI, class Src, int NT = kThreads>
 struct LoadKC {
   static constexpr int KQ = BK / 4;
-  static constexpr int NV = BX * KQ / kThreads;
-  static_assert(NV >= 1 && BX * KQ % kThreads == 0, "tile too small");
+  static constexpr int NV = BX * KQ / NT;
+  static_assert(NV >= 1 && BX * KQ % NT == 0, "tile too small");
   Src src;
   int64_t ld;
   int x0, xmax, kmax, kcur;
@@ -331,7 +331,7 @@ struct LoadKC {
     kcur = k0;
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       const int kq = idx % KQ, x = idx / KQ;
       const int gx = x0 + x, gk = k0 + 4 * kq;
       const int64_t o = static_cast<int64_t>(gx) * ld + gk;
@@ -348,7 +348,7 @@ struct LoadKC {
   __device__ __forceinline__ void store(f32x4* lds) const {
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       const int kq = idx % KQ, x = idx / KQ;
       f32x4 val = Src::fin(v[s]);
       if constexpr (TRI) {
@@ -364,7 +364,7 @@ struct LoadKC {
   __device__ __forceinline__ void store_bf(u32x2* hi, u32x2* lo) const {
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       const int kq = idx % KQ, x = idx / KQ;
       f32x4 val = Src::fin(v[s]);
       if constexpr (TRI) {
@@ -380,11 +380,11 @@ struct LoadKC {
 // Loader for a source whose output index is contiguous:
 // element (x, k) = src[k * ld + x].  Each thread reads a 4 (k) x 4 (x)
 // block as four float4 row pieces and transposes it in registers.
-template <int BX, int BK, bool VEC, class Src>
+template <int BX, int BK, bool VEC, class Src, int NT = kThreads>
 struct LoadXC {
   static constexpr int XQ = BX / 4;
   static constexpr int NB = XQ * (BK / 4);
-  static constexpr int NPT = (NB + kThreads - 1) / kThreads;
+  static constexpr int NPT = (NB + NT - 1) / NT;
   Src src;
   int64_t ld;
   int x0, xmax, kmax;
@@ -397,8 +397,8 @@ struct LoadXC {
   __device__ __forceinline__ void load(int k0) {
 #pragma unroll
     for (int s = 0; s < NPT; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (NB % kThreads != 0 && idx >= NB) continue;
+      const int idx = threadIdx.x + NT * s;
+      if (NB % NT != 0 && idx >= NB) continue;
       const int xq = idx % XQ, kg = idx / XQ;
       const int gx = x0 + 4 * xq;
 #pragma unroll
@@ -419,8 +419,8 @@ struct LoadXC {
   __device__ __forceinline__ void store(f32x4* lds) const {
 #pragma unroll
     for (int s = 0; s < NPT; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (NB % kThreads != 0 && idx >= NB) continue;
+      const int idx = threadIdx.x + NT * s;
+      if (NB % NT != 0 && idx >= NB) continue;
       const int xq = idx % XQ, kg = idx / XQ;
       f32x4 w[4];
 #pragma unroll
@@ -439,8 +439,8 @@ struct LoadXC {
   __device__ __forceinline__ void store_bf(u32x2* hi, u32x2* lo) const {
 #pragma unroll
     for (int s = 0; s < NPT; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (NB % kThreads != 0 && idx >= NB) continue;
+      const int idx = threadIdx.x + NT * s;
+      if (NB % NT != 0 && idx >= NB) continue;
       const int xq = idx % XQ, kg = idx / XQ;
       f32x4 w[4];
 #pragma unroll
@@ -636,6 +636,59 @@ __device__ __forceinline__ void mma_tile_bf3(const u32x4* ah, const u32x4* al, c
   }
 }
 
+// Wavefront grid of a BM x BN tile: GM x GN wavefronts (64 GM GN threads),
+// wavefront (wm, wn) = (wave / GN, wave % GN) owning FM x FN blocks of
+// 32 x 32 outputs.
+template <int BM_, int BN_, int GM_, int GN_>
+struct WGrid {
+  static constexpr int BM = BM_, BN = BN_, GM = GM_, GN = GN_;
+  static constexpr int NT = 64 * GM * GN;
+  static constexpr int TM = BM / GM, TN = BN / GN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "tile too small");
+  __device__ static int wm() { return (threadIdx.x >> 6) / GN; }
+  __device__ static int wn() { return (threadIdx.x >> 6) % GN; }
+  // row / column of accumulator register v of block (fm, fn) (32 x 32 MFMA
+  // output layout: lane l holds column l % 32, rows 8(v/4) + 4(l/32) + v%4)
+  __device__ static int row(int fm, int v) {
+    return wm() * TM + fm * 32 + 8 * (v >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (v & 3);
+  }
+  __device__ static int col(int fn) { return wn() * TN + fn * 32 + (threadIdx.x & 31); }
+};
+
+// mma_tile_bf3 for any wavefront grid.
+template <class W, int BK>
+__device__ __forceinline__ void mma_tile_bf3w(const u32x4* ah, const u32x4* al, const u32x4* bh,
+                                              const u32x4* bl, f32x16 (&acc)[W::FM][W::FN]) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, i = lane & 31;
+  const int wm = W::wm(), wn = W::wn();
+#pragma unroll
+  for (int q = 0; q < BK / 16; ++q) {
+    bf16x8 a_hi[W::FM], a_lo[W::FM], b_hi[W::FN], b_lo[W::FN];
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm) {
+      const int c = (2 * q + h) * BfShape<W::BM, BK>::PITCH + bf_swz(wm * W::TM + fm * 32 + i);
+      a_hi[fm] = __builtin_bit_cast(bf16x8, ah[c]);
+      a_lo[fm] = __builtin_bit_cast(bf16x8, al[c]);
+    }
+#pragma unroll
+    for (int fn = 0; fn < W::FN; ++fn) {
+      const int c = (2 * q + h) * BfShape<W::BN, BK>::PITCH + bf_swz(wn * W::TN + fn * 32 + i);
+      b_hi[fn] = __builtin_bit_cast(bf16x8, bh[c]);
+      b_lo[fn] = __builtin_bit_cast(bf16x8, bl[c]);
+    }
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < W::FN; ++fn) {
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo[fm], b_hi[fn], acc[fm][fn], 0, 0, 0);
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], b_lo[fn], acc[fm][fn], 0, 0, 0);
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], b_hi[fn], acc[fm][fn], 0, 0, 0);
+      }
+  }
+}
+
 // LDS bytes of one split-bfloat16 stage (A and B, hi and lo planes).
 template <int BM, int BN, int BK>
 constexpr int bf_stage_cells() {
@@ -688,6 +741,38 @@ __device__ __forceinline__ void pipeline2_bf(LA& a0, LA& a1, LB& b0, LB& b1, int
     __syncthreads();
   }
   if (nk & 1) compute(0);
+}
+
+// Two-stage split-bfloat16 pipeline for large tiles: LDS double-buffered,
+// one register set.  Tile kt+1's loads are issued before tile kt's MFMAs
+// and stored to the other LDS stage after them; one barrier per tile.
+// smem: 2 stages of bf_stage_cells() 16-byte cells.
+template <int BM, int BN, int BK, bool FULL, class LA, class LB, class MMA>
+__device__ __forceinline__ void pipeline_bf(LA& a, LB& b, int kbase, int nk, u32x4* smem,
+                                            MMA&& mma) {
+  constexpr int CA = BfShape<BM, BK>::CELLS, CB = BfShape<BN, BK>::CELLS;
+  constexpr int STAGE = 2 * (CA + CB);
+  auto store = [&](int st) {
+    u32x4* base = smem + st * STAGE;
+    a.store_bf(reinterpret_cast<u32x2*>(base), reinterpret_cast<u32x2*>(base + CA));
+    b.store_bf(reinterpret_cast<u32x2*>(base + 2 * CA), reinterpret_cast<u32x2*>(base + 2 * CA + CB));
+  };
+  if (nk <= 0) return;
+  a.template load<FULL>(kbase);
+  b.template load<FULL>(kbase);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) {
+      a.template load<FULL>(kbase + (kt + 1) * BK);
+      b.template load<FULL>(kbase + (kt + 1) * BK);
+    }
+    u32x4* base = smem + (kt & 1) * STAGE;
+    mma(base, base + CA, base + 2 * CA, base + 2 * CA + CB);
+    if (more) store((kt + 1) & 1);
+    __syncthreads();
+  }
 }
 
 template <int BM, int BN, int BK, bool FULL, class LA, class LB>

@@ -53,6 +53,7 @@ struct ClassRec {
   int m, n, r, rp;
   int first, count;
   int bn_r, bn_n, bg;
+  int bn_mv;   // M V tile: bn_r, or 256 (256 x 256 split-bfloat16 tiles)
   int s_mv, kl_mv, s_mtu, kl_mtu, s_gp, kl_gp, s_gw, kl_gw;
 };
 
@@ -154,6 +155,7 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
       k.bn_r = pick_bn(k.r);
       k.bn_n = kEpiBN;
       k.bg = pick_bn(k.r);
+      k.bn_mv = p.math && k.m >= 256 && k.r * 10 >= cdiv(k.r, 256) * 256 * 9 ? 256 : k.bn_r;
       p.cls.push_back(k);
     }
     cls_of[i] = c;
@@ -168,7 +170,8 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
   int64_t t_mv = 0, t_mtu = 0, t_gp = 0, t_gw = 0;
   for (auto& k : p.cls) {
     const int nt = cdiv(k.r, k.bg);
-    t_mv += static_cast<int64_t>(k.count) * cdiv(k.m, 128) * cdiv(k.r, k.bn_r);
+    const int bm_mv = k.bn_mv == 256 ? 256 : 128;
+    t_mv += static_cast<int64_t>(k.count) * cdiv(k.m, bm_mv) * cdiv(k.r, k.bn_mv);
     t_mtu += static_cast<int64_t>(k.count) * cdiv(k.n, 128) * cdiv(k.r, k.bn_r);
     t_gp += static_cast<int64_t>(k.count) * nt * (nt + 1) / 2;
   }
@@ -350,10 +353,10 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   // by every tile)
   DION_TRY(mk.mark(0, st));
   if (p.math) DION_TRY(split_t(p, base, 0, st));
-  for (int bn : {128, 64}) {
+  for (int bn : {256, 128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-      if (c.bn_r != bn) return false;
-      ci.tx = cdiv(c.m, 128);
+      if (c.bn_mv != bn) return false;
+      ci.tx = cdiv(c.m, bn == 256 ? 256 : 128);
       ci.ty = cdiv(c.r, bn);
       ci.splits = c.s_mv;
       ci.klen = c.kl_mv;

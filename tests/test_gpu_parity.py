@@ -48,6 +48,8 @@ def test_config1_ten_steps(gpu_lib, variant, arith):
 SHAPES = [
     (257, 129, 17), (129, 257, 33), (300, 200, 100), (64, 64, 64), (200, 96, 96),
     (1, 7, 1), (9, 1, 1), (131, 67, 3), (512, 384, 128), (130, 390, 65), (1000, 37, 20),
+    # ranks that take the 256 x 256 split-bfloat16 M V tiles, ragged in m, n and r
+    (700, 300, 250), (520, 1000, 480),
 ]
 
 
