@@ -54,6 +54,7 @@ struct ClassRec {
   int first, count;
   int bn_r, bn_n, bg;
   int bn_mv;   // M V tile: bn_r, or 256 (256 x 256 split-bfloat16 tiles)
+  int bn_mtu;  // M^T U tile, likewise
   int s_mv, kl_mv, s_mtu, kl_mtu, s_gp, kl_gp, s_gw, kl_gw;
 };
 
@@ -155,7 +156,9 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
       k.bn_r = pick_bn(k.r);
       k.bn_n = kEpiBN;
       k.bg = pick_bn(k.r);
-      k.bn_mv = p.math && k.m >= 256 && k.r * 10 >= cdiv(k.r, 256) * 256 * 9 ? 256 : k.bn_r;
+      const bool big_r = k.r * 10 >= cdiv(k.r, 256) * 256 * 9;   // <= 10% of 256-wide tiles idle
+      k.bn_mv = p.math && k.m >= 256 && big_r ? 256 : k.bn_r;
+      k.bn_mtu = p.math && k.n >= 256 && big_r ? 256 : k.bn_r;
       p.cls.push_back(k);
     }
     cls_of[i] = c;
@@ -172,7 +175,8 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     const int nt = cdiv(k.r, k.bg);
     const int bm_mv = k.bn_mv == 256 ? 256 : 128;
     t_mv += static_cast<int64_t>(k.count) * cdiv(k.m, bm_mv) * cdiv(k.r, k.bn_mv);
-    t_mtu += static_cast<int64_t>(k.count) * cdiv(k.n, 128) * cdiv(k.r, k.bn_r);
+    const int bm_mtu = k.bn_mtu == 256 ? 256 : 128;
+    t_mtu += static_cast<int64_t>(k.count) * cdiv(k.n, bm_mtu) * cdiv(k.r, k.bn_mtu);
     t_gp += static_cast<int64_t>(k.count) * nt * (nt + 1) / 2;
   }
   t_gw = t_gp;
@@ -380,10 +384,10 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   // W = M^T U (split-bfloat16: U^T split once into planes, read as whole
   // cells by every tile)
   if (p.math) DION_TRY(split_t(p, base, 1, st));
-  for (int bn : {128, 64}) {
+  for (int bn : {256, 128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-      if (c.bn_r != bn) return false;
-      ci.tx = cdiv(c.n, 128);
+      if (c.bn_mtu != bn) return false;
+      ci.tx = cdiv(c.n, bn == 256 ? 256 : 128);
       ci.ty = cdiv(c.r, bn);
       ci.splits = c.s_mtu;
       ci.klen = c.kl_mtu;

@@ -422,6 +422,50 @@ __global__ __launch_bounds__(kBigThreads) void k_mv3b(Launch L) {
   else mv3b_body<GT, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
 }
 
+// M^T U on the same 256 x 256 tiles (output rows: n, columns: r).
+template <typename GT, bool VEC, bool FULL>
+__device__ __forceinline__ void mtu3b_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
+                                           int s, int tm, int tn, int kbeg, int kend, u32x4* smem) {
+  constexpr int BK = 32;
+  const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
+  LoadXC<WB::BM, BK, VEC, SrcM<GT>, WB::NT> la(sm, d.n, tm * WB::BM, d.n, kend);
+  const uint16_t* ut = reinterpret_cast<const uint16_t*>(L.ws + d.oH);
+  LoadPl<WB::BN, BK, WB::NT> lb(ut, ut + static_cast<int64_t>(d.r) * plane_pitch(d.m), d.r,
+                                tn * WB::BN, d.r);
+  f32x16 acc[WB::FM][WB::FN];
+  zero_acc(acc);
+  pipeline_bf<WB::BM, WB::BN, BK, FULL>(
+      la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem,
+      [&](const u32x4* ah, const u32x4* al, const u32x4* bh, const u32x4* bl) {
+        mma_tile_bf3w<WB, BK>(ah, al, bh, bl, acc);
+      });
+  float* out = ci.splits == 1
+                   ? reinterpret_cast<float*>(L.ws + d.oW)
+                   : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.n * d.r;
+  store_tile_w<WB>(out, d.r, tm * WB::BM, tn * WB::BN, d.n, d.r, acc);
+}
+
+template <typename GT, bool VEC>
+__global__ __launch_bounds__(kBigThreads) void k_mtu3b(Launch L) {
+  constexpr int BK = 32;
+  __shared__ u32x4 smem[2 * bf_stage_cells<WB::BM, WB::BN, BK>()];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int per = ci.tx * ci.ty;
+  const int s = local / per;
+  int tm, tn;
+  tile_order(local - s * per, ci.tx, ci.ty, tm, tn);
+  const int kbeg = s * ci.klen;
+  const int kend = min(d.m, kbeg + ci.klen);
+  const bool full = VEC && (tm + 1) * WB::BM <= d.n && (tn + 1) * WB::BN <= d.r &&
+                    (kend - kbeg) % BK == 0;
+  if (full) mtu3b_body<GT, VEC, true>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+  else mtu3b_body<GT, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+}
+
 template <typename GT, int BN, bool VEC, bool FULL>
 __device__ __forceinline__ void mtu3_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
                                           int s, int tm, int tn, int kbeg, int kend, u32x4* smem) {
@@ -593,6 +637,12 @@ hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, int math, hi
 }
 
 hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st) {
+  if (bn == 256) {   // split-bfloat16 only
+    constexpr int T = kBigThreads;
+    if (gdtype == 0)
+      return vec ? go(k_mtu3b<float, true>, L, st, T) : go(k_mtu3b<float, false>, L, st, T);
+    return vec ? go(k_mtu3b<uint16_t, true>, L, st, T) : go(k_mtu3b<uint16_t, false>, L, st, T);
+  }
   DION_DISPATCH(k_mtu)
 }
 

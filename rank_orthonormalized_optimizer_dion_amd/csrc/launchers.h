@@ -7,7 +7,7 @@
 namespace dion {
 
 // gdtype: 0 = float32 G, 1 = bfloat16 G.  bn: output tile width (64 or 128;
-// launch_mv also 256: 256 x 256 tiles, split-bfloat16 only).
+// launch_mv and launch_mtu also 256: 256 x 256 tiles, split-bfloat16 only).
 // vec: every operand of the launch admits 16-byte vector loads.
 // math: 0 = float32 MFMA products, 1 = split-bfloat16 (three bf16 MFMAs).
 hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st);
