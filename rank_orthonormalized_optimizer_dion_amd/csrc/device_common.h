@@ -689,6 +689,47 @@ __device__ __forceinline__ void mma_tile_bf3w(const u32x4* ah, const u32x4* al, 
   }
 }
 
+// Two products sharing the left operand, A B^T and A C^T (the fused X / R
+// update): A's fragments are read from LDS once per 16 k for both.
+template <class W, int BK>
+__device__ __forceinline__ void mma_tile_bf3w2(const u32x4* ah, const u32x4* al, const u32x4* bh,
+                                               const u32x4* bl, const u32x4* ch, const u32x4* cl,
+                                               f32x16 (&ab)[W::FM][W::FN],
+                                               f32x16 (&ac)[W::FM][W::FN]) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, i = lane & 31;
+  const int wm = W::wm(), wn = W::wn();
+#pragma unroll
+  for (int q = 0; q < BK / 16; ++q) {
+    bf16x8 a_hi[W::FM], a_lo[W::FM], b_hi[W::FN], b_lo[W::FN], c_hi[W::FN], c_lo[W::FN];
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm) {
+      const int c = (2 * q + h) * BfShape<W::BM, BK>::PITCH + bf_swz(wm * W::TM + fm * 32 + i);
+      a_hi[fm] = __builtin_bit_cast(bf16x8, ah[c]);
+      a_lo[fm] = __builtin_bit_cast(bf16x8, al[c]);
+    }
+#pragma unroll
+    for (int fn = 0; fn < W::FN; ++fn) {
+      const int c = (2 * q + h) * BfShape<W::BN, BK>::PITCH + bf_swz(wn * W::TN + fn * 32 + i);
+      b_hi[fn] = __builtin_bit_cast(bf16x8, bh[c]);
+      b_lo[fn] = __builtin_bit_cast(bf16x8, bl[c]);
+      c_hi[fn] = __builtin_bit_cast(bf16x8, ch[c]);
+      c_lo[fn] = __builtin_bit_cast(bf16x8, cl[c]);
+    }
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < W::FN; ++fn) {
+        ab[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo[fm], b_hi[fn], ab[fm][fn], 0, 0, 0);
+        ac[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo[fm], c_hi[fn], ac[fm][fn], 0, 0, 0);
+        ab[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], b_lo[fn], ab[fm][fn], 0, 0, 0);
+        ac[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], c_lo[fn], ac[fm][fn], 0, 0, 0);
+        ab[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], b_hi[fn], ab[fm][fn], 0, 0, 0);
+        ac[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], c_hi[fn], ac[fm][fn], 0, 0, 0);
+      }
+  }
+}
+
 // LDS bytes of one split-bfloat16 stage (A and B, hi and lo planes).
 template <int BM, int BN, int BK>
 constexpr int bf_stage_cells() {

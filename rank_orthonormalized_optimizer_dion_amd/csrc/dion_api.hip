@@ -154,7 +154,9 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
       k.r = static_cast<int>(mats[i].r);
       k.rp = cdiv(k.r, kCholNB) * kCholNB;
       k.bn_r = pick_bn(k.r);
-      k.bn_n = kEpiBN;
+      // update tile: 256 x 128 split-bfloat16 tiles (bn_n = 256) when rows
+      // fill them to 90%
+      k.bn_n = p.math && k.m * 10 >= cdiv(k.m, 256) * 256 * 9 && k.n >= 128 ? 256 : kEpiBN;
       k.bg = pick_bn(k.r);
       const bool big_r = k.r * 10 >= cdiv(k.r, 256) * 256 * 9;   // <= 10% of 256-wide tiles idle
       k.bn_mv = p.math && k.m >= 256 && big_r ? 256 : k.bn_r;
@@ -421,11 +423,11 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
 
   // X and R
   DION_TRY(mk.mark(4, st));
-  for (int bn : {128, 64}) {
+  for (int bn : {256, 128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_n != bn) return false;
-      ci.tx = cdiv(c.m, 128);
-      ci.ty = cdiv(c.n, bn);
+      ci.tx = cdiv(c.m, bn == 256 ? 256 : 128);
+      ci.ty = cdiv(c.n, bn == 256 ? 128 : bn);
       ci.tiles = ci.tx * ci.ty;
       return true;
     }, [&](const Launch& L) { return launch_epi(L, p.gdtype, bn, p.vec, p.math, st); }));

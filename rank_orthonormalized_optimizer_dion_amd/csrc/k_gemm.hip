@@ -510,6 +510,92 @@ __global__ __launch_bounds__(kThreads, 2) void k_mtu3(Launch L) {
   else mtu3_body<GT, BN, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
 }
 
+// Fused X / R update on 256 x 128 tiles: 8 wavefronts (4 x 2) of 64 x 64,
+// two per SIMD, each holding both products (U Vbar^T, U W^T).
+using WE = WGrid<256, 128, 4, 2>;
+
+template <typename GT, bool VEC, bool FULL>
+__device__ __forceinline__ void epi3b_body(const Launch& L, const MatDesc& d, int tm, int tn,
+                                           u32x4* smem) {
+  constexpr int BK = 32;
+  constexpr int CA = BfShape<WE::BM, BK>::CELLS, CB = BfShape<WE::BN, BK>::CELLS;
+  constexpr int STAGE = 2 * (CA + 2 * CB);
+  const float* U = reinterpret_cast<const float*>(L.ws + d.oB);
+  const float* Wf = reinterpret_cast<const float*>(L.ws + d.oW);
+  LoadKC<WE::BM, BK, VEC, false, SrcF32, WE::NT> la(SrcF32{U}, d.r, tm * WE::BM, d.m, d.r);
+  LoadKC<WE::BN, BK, VEC, false, SrcF32, WE::NT> lv(SrcF32{d.V}, d.r, tn * WE::BN, d.n, d.r);
+  LoadKC<WE::BN, BK, VEC, false, SrcF32, WE::NT> lw(SrcF32{Wf}, d.r, tn * WE::BN, d.n, d.r);
+  f32x16 ax[WE::FM][WE::FN], ar[WE::FM][WE::FN];
+  zero_acc(ax);
+  zero_acc(ar);
+  // stage layout: A hi, A lo, V hi, V lo, W hi, W lo; LDS double-buffered,
+  // the next tile's loads in flight during this tile's MFMAs
+  auto store = [&](int st) {
+    u32x4* b = smem + st * STAGE;
+    la.store_bf(reinterpret_cast<u32x2*>(b), reinterpret_cast<u32x2*>(b + CA));
+    lv.store_bf(reinterpret_cast<u32x2*>(b + 2 * CA), reinterpret_cast<u32x2*>(b + 2 * CA + CB));
+    lw.store_bf(reinterpret_cast<u32x2*>(b + 2 * CA + 2 * CB),
+                reinterpret_cast<u32x2*>(b + 2 * CA + 3 * CB));
+  };
+  auto load = [&](int k0) {
+    la.template load<FULL>(k0);
+    lv.template load<FULL>(k0);
+    lw.template load<FULL>(k0);
+  };
+  const int nk = (d.r + BK - 1) / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) load((kt + 1) * BK);
+    const u32x4* b = smem + (kt & 1) * STAGE;
+    mma_tile_bf3w2<WE, BK>(b, b + CA, b + 2 * CA, b + 2 * CA + CB, b + 2 * CA + 2 * CB,
+                           b + 2 * CA + 3 * CB, ax, ar);
+    if (more) store((kt + 1) & 1);
+    __syncthreads();
+  }
+  gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
+  gptr<float> X = to_global(d.X);
+  gptr<float> R = to_global(d.R);
+  const float eta = L.eta, beta = L.beta;
+#pragma unroll
+  for (int fm = 0; fm < WE::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < WE::FN; ++fn) {
+      const int col = tn * WE::BN + WE::col(fn);
+      if (!FULL && col >= d.n) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = tm * WE::BM + WE::row(fm, v);
+        if (!FULL && row >= d.m) continue;
+        const int64_t o = static_cast<int64_t>(row) * d.n + col;
+        float g;
+        if constexpr (sizeof(GT) == 2) g = bf16_to_f32(G[o]); else g = G[o];
+        const float mv = g + R[o];
+        X[o] = X[o] - eta * ax[fm][fn][v];
+        R[o] = beta * (mv - ar[fm][fn][v]);
+      }
+    }
+}
+
+template <typename GT, bool VEC>
+__global__ __launch_bounds__(kBigThreads) void k_epi3b(Launch L) {
+  constexpr int BK = 32;
+  constexpr int STAGE = 2 * (BfShape<WE::BM, BK>::CELLS + 2 * BfShape<WE::BN, BK>::CELLS);
+  __shared__ u32x4 smem[2 * STAGE];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  int tm, tn;
+  tile_order(local, ci.tx, ci.ty, tm, tn);
+  const bool full = VEC && (tm + 1) * WE::BM <= d.m && (tn + 1) * WE::BN <= d.n && d.r % BK == 0;
+  if (full) epi3b_body<GT, VEC, true>(L, d, tm, tn, smem);
+  else epi3b_body<GT, VEC, false>(L, d, tm, tn, smem);
+}
+
 template <typename GT, int BN, bool VEC, bool FULL>
 __device__ __forceinline__ void epi3_body(const Launch& L, const MatDesc& d, int tm, int tn,
                                           u32x4* smem) {
@@ -657,6 +743,12 @@ hipError_t launch_trmm(const Launch& L, int bn, bool vec, hipStream_t st) {
 }
 
 hipError_t launch_epi(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st) {
+  if (bn == 256) {   // split-bfloat16 only: 256 x 128 tiles
+    constexpr int T = kBigThreads;
+    if (gdtype == 0)
+      return vec ? go(k_epi3b<float, true>, L, st, T) : go(k_epi3b<float, false>, L, st, T);
+    return vec ? go(k_epi3b<uint16_t, true>, L, st, T) : go(k_epi3b<uint16_t, false>, L, st, T);
+  }
   DION_DISPATCH(k_epi)
 }
 
