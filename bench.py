@@ -249,10 +249,13 @@ def main(argv=None) -> int:
                             wl.eta, wl.beta, args.math)
     f, b = phase_model(shapes, args.variant, eg)
     dom = max(phases, key=phases.get)
-    kernel = {"mv": "k_mv", "orth_p": "orth(P)", "mtu": "k_mtu", "right": "right factor",
-              "update": "k_epi"}[dom]
-    if args.math == "bf16x3" and kernel in ("k_mv", "k_mtu", "k_epi"):
-        kernel += "3"
+    # kernels of each phase on this stack (every class takes the large
+    # split-bfloat16 tiles: rows and ranks are multiples of 256)
+    names = {"mv": "k_mv", "orth_p": "orth(P)", "mtu": "k_mtu", "right": "right factor",
+             "update": "k_epi"}
+    if args.math == "bf16x3":
+        names.update(mv="k_mv3b", mtu="k_mtu3b", update="k_epi3b")
+    kernel = names[dom]
     traffic = measured_traffic(kernel, wl.name) if kernel.startswith("k_") else None
     roof = roofline_of(dom, phases[dom], f, b, traffic, args.math)
     roof["kernel"] = kernel
