@@ -255,6 +255,48 @@ __device__ __forceinline__ int64_t plane_cell(int64_t rows, int x, int k8) {
   return ((k8 / CB) * rows + x) * CB + k8 % CB;
 }
 
+// Cell (x, k8) of a split-bfloat16 plane with `rows` rows in row-major cell
+// order: the cells of one reduction column k8 of all rows are contiguous,
+// so 64 consecutive rows of one k8 are one 1 KB run (one direct-to-LDS
+// wavefront load).
+__device__ __forceinline__ int64_t plane_cell_r(int64_t rows, int x, int k8) {
+  return static_cast<int64_t>(k8) * rows + x;
+}
+
+// Direct-to-LDS loader of a plane pair (hi, lo) in plane_cell_r order:
+// the BX rows x0 .. x0 + BX - 1 and BK / 8 reduction cells of one tile go
+// straight into the BfShape LDS layout with global_load_lds_dwordx4, one
+// wavefront instruction per 64 cells, no registers and no conversion.
+// Lane l of a 64-cell chunk c fetches row bf_swz(64 c + l), which the
+// swizzled layout keeps at LDS cell 64 c + l.  Rows past xmax read row
+// xmax - 1: they only feed outputs that are never stored.
+template <int BX, int BK, int NT>
+struct LoadDma {
+  static constexpr int K8 = BK / 8, CH = BX / 64;
+  static constexpr int NI = 2 * K8 * CH;   // wavefront instructions per tile
+  static constexpr int PER = NI / (NT / 64);
+  static_assert(BX % 64 == 0 && NI % (NT / 64) == 0, "tile does not split over the wavefronts");
+  const u32x4* hi;
+  const u32x4* lo;
+  int64_t rows;
+  int x0, xmax;
+
+  __device__ __forceinline__ void issue(int k0, u32x4* lds_hi, u32x4* lds_lo) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = wave * PER + j;
+      const int plane = i / (K8 * CH), rem = i % (K8 * CH);
+      const int k8 = rem / CH, c = rem % CH;
+      const int x = min(x0 + bf_swz(64 * c + lane), xmax - 1);
+      const u32x4* src = (plane ? lo : hi) + plane_cell_r(rows, x, k0 / 8 + k8);
+      u32x4* dst = (plane ? lds_lo : lds_hi) + k8 * BfShape<BX, BK>::PITCH + 64 * c;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                       (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
+    }
+  }
+};
+
 // Loader of split-bfloat16 planes written ahead of time (hi and lo, zero
 // past the reduction length) in the K-blocked cell order of plane_cell():
 // the BK = kPlaneK slice of BX consecutive rows is one contiguous run of

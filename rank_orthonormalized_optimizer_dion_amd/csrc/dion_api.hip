@@ -232,6 +232,7 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     const size_t kpart = std::max(k.s_mv > 1 ? k.s_mv * m * r : 0, k.s_mtu > 1 ? k.s_mtu * n * r : 0);
     d.oK = kpart ? take(kpart * 4) : 0;
     d.oH = p.math ? take(r * std::max(plane_pitch(k.m), plane_pitch(k.n)) * 4) : 0;
+    d.oE = k.bn_n == 256 ? take((m + 2 * n) * plane_pitch(k.r) * 4) : 0;
     p.table[g] = d;
   }
   p.ws_bytes = off;
@@ -421,8 +422,14 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
     }, [&](const Launch& L) { return launch_colscale(L, st); }));
   }
 
-  // X and R
+  // X and R (large split-bfloat16 tiles: U, W, Vbar split into planes first)
   DION_TRY(mk.mark(4, st));
+  DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+    if (c.bn_n != 256) return false;
+    const int cr = cdiv(c.r, kSplitTile);
+    ci.tiles = (cdiv(c.m, kSplitTile) + 2 * cdiv(c.n, kSplitTile)) * cr;
+    return true;
+  }, [&](const Launch& L) { return launch_split_n(L, st); }));
   for (int bn : {256, 128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_n != bn) return false;

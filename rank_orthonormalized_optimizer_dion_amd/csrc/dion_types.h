@@ -32,6 +32,9 @@ struct MatDesc {
   int64_t oD;        // kCholNB^2 + rp float64: diagonal-block inverse, diag(S)
   int64_t oN;        // r          float32: inverse column norms (Dion)
   int64_t oK;        // split-K partial products (float32)
+  int64_t oE;        // split-bfloat16 planes (hi, then lo) of U (m rows), W
+                     // and Vbar (n rows) for the fused update, row-major
+                     // cells (plane_cell_r), pitch plane_pitch(r); 0 if unused
   int64_t oH;        // split-bfloat16 planes (hi, then lo) of V^T during
                      // M V, of U^T during M^T U: r x plane_pitch(rows)
                      // bfloat16 each, zero past the last row; 0 without them

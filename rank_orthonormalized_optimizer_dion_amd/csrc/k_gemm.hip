@@ -511,72 +511,85 @@ __global__ __launch_bounds__(kThreads, 2) void k_mtu3(Launch L) {
 }
 
 // Fused X / R update on 256 x 128 tiles: 8 wavefronts (4 x 2) of 64 x 64,
-// two per SIMD, each holding both products (U Vbar^T, U W^T).
+// two per SIMD, each holding both products (U Vbar^T, U W^T).  The rank-r
+// factors come as split-bfloat16 planes written by k_split_n and are copied
+// straight into LDS.
 using WE = WGrid<256, 128, 4, 2>;
 
 template <typename GT, bool VEC, bool FULL>
 __device__ __forceinline__ void epi3b_body(const Launch& L, const MatDesc& d, int tm, int tn,
                                            u32x4* smem) {
   constexpr int BK = 32;
+  static_assert(kPlaneK % BK == 0, "planes hold whole reduction tiles");
   constexpr int CA = BfShape<WE::BM, BK>::CELLS, CB = BfShape<WE::BN, BK>::CELLS;
   constexpr int STAGE = 2 * (CA + 2 * CB);
-  const float* U = reinterpret_cast<const float*>(L.ws + d.oB);
-  const float* Wf = reinterpret_cast<const float*>(L.ws + d.oW);
-  LoadKC<WE::BM, BK, VEC, false, SrcF32, WE::NT> la(SrcF32{U}, d.r, tm * WE::BM, d.m, d.r);
-  LoadKC<WE::BN, BK, VEC, false, SrcF32, WE::NT> lv(SrcF32{d.V}, d.r, tn * WE::BN, d.n, d.r);
-  LoadKC<WE::BN, BK, VEC, false, SrcF32, WE::NT> lw(SrcF32{Wf}, d.r, tn * WE::BN, d.n, d.r);
+  // split-bfloat16 planes of U (m rows), W and Vbar (n rows), plane_cell_r
+  // order, zero past column r
+  const int rq = plane_pitch(d.r);
+  const u32x4* pu = reinterpret_cast<const u32x4*>(L.ws + d.oE);
+  const int64_t cu = static_cast<int64_t>(d.m) * (rq / 8), cn = static_cast<int64_t>(d.n) * (rq / 8);
+  const u32x4* pw = pu + 2 * cu;
+  const u32x4* pv = pw + 2 * cn;
+  const LoadDma<WE::BM, BK, WE::NT> la{pu, pu + cu, d.m, tm * WE::BM, d.m};
+  const LoadDma<WE::BN, BK, WE::NT> lv{pv, pv + cn, d.n, tn * WE::BN, d.n};
+  const LoadDma<WE::BN, BK, WE::NT> lw{pw, pw + cn, d.n, tn * WE::BN, d.n};
   f32x16 ax[WE::FM][WE::FN], ar[WE::FM][WE::FN];
   zero_acc(ax);
   zero_acc(ar);
-  // stage layout: A hi, A lo, V hi, V lo, W hi, W lo; LDS double-buffered,
-  // the next tile's loads in flight during this tile's MFMAs
-  auto store = [&](int st) {
-    u32x4* b = smem + st * STAGE;
-    la.store_bf(reinterpret_cast<u32x2*>(b), reinterpret_cast<u32x2*>(b + CA));
-    lv.store_bf(reinterpret_cast<u32x2*>(b + 2 * CA), reinterpret_cast<u32x2*>(b + 2 * CA + CB));
-    lw.store_bf(reinterpret_cast<u32x2*>(b + 2 * CA + 2 * CB),
-                reinterpret_cast<u32x2*>(b + 2 * CA + 3 * CB));
+  // stage layout: A hi, A lo, V hi, V lo, W hi, W lo; double-buffered: the
+  // next tile's copies run during this tile's MFMAs and are waited for at
+  // the barrier that ends it
+  auto issue = [&](int k0, u32x4* b) {
+    la.issue(k0, b, b + CA);
+    lv.issue(k0, b + 2 * CA, b + 2 * CA + CB);
+    lw.issue(k0, b + 2 * CA + 2 * CB, b + 2 * CA + 3 * CB);
   };
-  auto load = [&](int k0) {
-    la.template load<FULL>(k0);
-    lv.template load<FULL>(k0);
-    lw.template load<FULL>(k0);
-  };
-  const int nk = (d.r + BK - 1) / BK;
-  load(0);
-  store(0);
+  const int nk = rq / BK;
+  issue(0, smem);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load((kt + 1) * BK);
+    if (kt + 1 < nk) issue((kt + 1) * BK, smem + ((kt + 1) & 1) * STAGE);
     const u32x4* b = smem + (kt & 1) * STAGE;
     mma_tile_bf3w2<WE, BK>(b, b + CA, b + 2 * CA, b + 2 * CA + CB, b + 2 * CA + 2 * CB,
                            b + 2 * CA + 3 * CB, ax, ar);
-    if (more) store((kt + 1) & 1);
     __syncthreads();
   }
   gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
   gptr<float> X = to_global(d.X);
   gptr<float> R = to_global(d.R);
   const float eta = L.eta, beta = L.beta;
+  // Eight elements of a 32 x 32 block at a time: every load of a batch is
+  // issued before its first store (X, G and R may alias as far as the
+  // compiler knows, so loads interleaved with stores would run one element
+  // at a time).  m n < 2^31 (checked at the boundary): offsets are 32-bit.
 #pragma unroll
   for (int fm = 0; fm < WE::FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < WE::FN; ++fn) {
-      const int col = tn * WE::BN + WE::col(fn);
-      if (!FULL && col >= d.n) continue;
+    for (int fn = 0; fn < WE::FN; ++fn)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = tm * WE::BM + WE::row(fm, v);
-        if (!FULL && row >= d.m) continue;
-        const int64_t o = static_cast<int64_t>(row) * d.n + col;
-        float g;
-        if constexpr (sizeof(GT) == 2) g = bf16_to_f32(G[o]); else g = G[o];
-        const float mv = g + R[o];
-        X[o] = X[o] - eta * ax[fm][fn][v];
-        R[o] = beta * (mv - ar[fm][fn][v]);
+      for (int h = 0; h < 16; h += 8) {
+        const int col = tn * WE::BN + WE::col(fn);
+        float gv[8], rv[8], xv[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int row = tm * WE::BM + WE::row(fm, h + v);
+          if (FULL || (row < d.m && col < d.n)) {
+            const unsigned o = static_cast<unsigned>(row * d.n + col);
+            if constexpr (sizeof(GT) == 2) gv[v] = bf16_to_f32(G[o]); else gv[v] = G[o];
+            rv[v] = R[o];
+            xv[v] = X[o];
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int row = tm * WE::BM + WE::row(fm, h + v);
+          if (FULL || (row < d.m && col < d.n)) {
+            const unsigned o = static_cast<unsigned>(row * d.n + col);
+            X[o] = xv[v] - eta * ax[fm][fn][h + v];
+            R[o] = beta * ((gv[v] + rv[v]) - ar[fm][fn][h + v]);
+          }
+        }
       }
-    }
 }
 
 template <typename GT, bool VEC>
@@ -591,7 +604,7 @@ __global__ __launch_bounds__(kBigThreads) void k_epi3b(Launch L) {
   if (skipped(L, d)) return;
   int tm, tn;
   tile_order(local, ci.tx, ci.ty, tm, tn);
-  const bool full = VEC && (tm + 1) * WE::BM <= d.m && (tn + 1) * WE::BN <= d.n && d.r % BK == 0;
+  const bool full = (tm + 1) * WE::BM <= d.m && (tn + 1) * WE::BN <= d.n;
   if (full) epi3b_body<GT, VEC, true>(L, d, tm, tn, smem);
   else epi3b_body<GT, VEC, false>(L, d, tm, tn, smem);
 }

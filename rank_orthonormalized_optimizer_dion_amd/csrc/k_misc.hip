@@ -3,6 +3,7 @@
 //   k_colnorm   Dion's rule, part 1: inverse Euclidean norms of W's columns
 //   k_colscale  Dion's rule, part 2: Vbar = W diag(1/||w_j||) written into V
 //   k_split_t   split-bfloat16 planes of V^T for M V, of U^T for M^T U
+//   k_split_n   split-bfloat16 planes of U, W and Vbar for the fused update
 // (right-factor rule of the Orth-Dion page's closing remark; column scaling
 // as the Orth-Dion abstract describes it).
 #include <math.h>
@@ -155,6 +156,86 @@ __global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
   }
 }
 
+// U (m x r), W and Vbar (n x r) as hi / lo bfloat16 planes in plane_cell_r
+// order (cell (x, k8): elements 8 k8 .. 8 k8 + 7 of row x), zero in columns
+// r .. plane_pitch(r), split as BfShape describes.  One workgroup per 64 x 64
+// tile of a factor: coalesced float4 row reads into LDS, then each thread
+// splits two cells; consecutive threads write consecutive rows of one k8.
+__global__ __launch_bounds__(kThreads) void k_split_n(Launch L) {
+  constexpr int T = kSplitTile;
+  __shared__ float tile[T][T + 1];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int cr = (d.r + T - 1) / T;
+  const int tu = (d.m + T - 1) / T * cr, tv = (d.n + T - 1) / T * cr;
+  const int rq = plane_pitch(d.r);
+  const int64_t cu = static_cast<int64_t>(d.m) * (rq / 8), cn = static_cast<int64_t>(d.n) * (rq / 8);
+  u32x4* out = reinterpret_cast<u32x4*>(L.ws + d.oE);
+  const float* src;
+  int rows, t = local;
+  int64_t plane;
+  if (t < tu) {
+    src = reinterpret_cast<const float*>(L.ws + d.oB);
+    rows = d.m;
+    plane = cu;
+  } else if ((t -= tu) < tv) {
+    src = reinterpret_cast<const float*>(L.ws + d.oW);
+    rows = d.n;
+    plane = cn;
+    out += 2 * cu;
+  } else {
+    t -= tv;
+    src = d.V;
+    rows = d.n;
+    plane = cn;
+    out += 2 * cu + 2 * cn;
+  }
+  const int i0 = (t / cr) * T, j0 = (t % cr) * T;
+  gptr<const float> Q = to_global(src);
+  const bool vec = (d.r & 3) == 0;
+#pragma unroll
+  for (int s = 0; s < T * T / 4 / kThreads; ++s) {
+    const int e = threadIdx.x + kThreads * s;
+    const int i = e / (T / 4), j = 4 * (e % (T / 4));
+    const int gi = i0 + i, gj = j0 + j;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (gi < rows) {
+      const int64_t o = static_cast<int64_t>(gi) * d.r + gj;
+      if (vec && gj + 3 < d.r) {
+        v = *(gptr<const f32x4>)(Q + o);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = gj + c < d.r ? Q[o + c] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) tile[i][j + c] = v[c];
+  }
+  __syncthreads();
+  gptr<u32x4> po = to_global(out);
+#pragma unroll
+  for (int s = 0; s < T * T / 8 / kThreads; ++s) {
+    const int c = threadIdx.x + kThreads * s;
+    const int x = c % T, k8 = c / T;
+    if (i0 + x >= rows || j0 + 8 * k8 >= rq) continue;
+    f32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = tile[x][8 * k8 + e];
+      b[e] = tile[x][8 * k8 + 4 + e];
+    }
+    u32x2 ha, la, hb, lb;
+    bf_split4(a, ha, la);
+    bf_split4(b, hb, lb);
+    const int64_t o = plane_cell_r(rows, i0 + x, j0 / 8 + k8);
+    po[o] = u32x4{ha.x, ha.y, hb.x, hb.y};
+    po[plane + o] = u32x4{la.x, la.y, lb.x, lb.y};
+  }
+}
+
 template <class K>
 hipError_t go(K kernel, const Launch& L, hipStream_t st) {
   if (L.total <= 0) return hipSuccess;
@@ -169,5 +250,6 @@ hipError_t launch_reduce(const Launch& L, hipStream_t st) { return go(k_reduce, 
 hipError_t launch_colnorm(const Launch& L, hipStream_t st) { return go(k_colnorm, L, st); }
 hipError_t launch_colscale(const Launch& L, hipStream_t st) { return go(k_colscale, L, st); }
 hipError_t launch_split_t(const Launch& L, hipStream_t st) { return go(k_split_t, L, st); }
+hipError_t launch_split_n(const Launch& L, hipStream_t st) { return go(k_split_n, L, st); }
 
 }  // namespace dion

@@ -29,6 +29,9 @@ hipError_t launch_colscale(const Launch& L, hipStream_t st);
 // kSplitTile x kSplitTile tiles of V or U
 constexpr int kSplitTile = 64;
 hipError_t launch_split_t(const Launch& L, hipStream_t st);
+// U, W and Vbar split-bfloat16 planes for the large-tile fused update, in
+// kSplitTile x kSplitTile tiles of each factor
+hipError_t launch_split_n(const Launch& L, hipStream_t st);
 int elems_per_tile();
 
 }  // namespace dion
