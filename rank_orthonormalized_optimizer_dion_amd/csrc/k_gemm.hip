@@ -34,6 +34,51 @@ __device__ __forceinline__ void store_tile(float* out_, int64_t ld, int r0, int 
     }
 }
 
+// The fused update's epilogue for a tile at (r0, c0) whose accumulators
+// hold U Vbar^T (ax) and U W^T (ar) in the 32 x 32 MFMA layout of wavefront
+// grid W: X -= eta ax, R = beta ((G + R) - ar).  Eight elements at a time,
+// every load of a batch issued before its first store (X, G and R may alias
+// as far as the compiler knows, so loads interleaved with stores would run
+// one element at a time).  m n < 2^31 (checked at the boundary): offsets
+// are 32-bit.
+template <class W, typename GT, bool FULL>
+__device__ __forceinline__ void update_epilogue(const Launch& L, const MatDesc& d, int r0, int c0,
+                                                const f32x16 (&ax)[W::FM][W::FN],
+                                                const f32x16 (&ar)[W::FM][W::FN]) {
+  gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
+  gptr<float> X = to_global(d.X);
+  gptr<float> R = to_global(d.R);
+  const float eta = L.eta, beta = L.beta;
+#pragma unroll
+  for (int fm = 0; fm < W::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < W::FN; ++fn)
+#pragma unroll
+      for (int h = 0; h < 16; h += 8) {
+        const int col = c0 + W::col(fn);
+        float gv[8], rv[8], xv[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int row = r0 + W::row(fm, h + v);
+          if (FULL || (row < d.m && col < d.n)) {
+            const unsigned o = static_cast<unsigned>(row * d.n + col);
+            if constexpr (sizeof(GT) == 2) gv[v] = bf16_to_f32(G[o]); else gv[v] = G[o];
+            rv[v] = R[o];
+            xv[v] = X[o];
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int row = r0 + W::row(fm, h + v);
+          if (FULL || (row < d.m && col < d.n)) {
+            const unsigned o = static_cast<unsigned>(row * d.n + col);
+            X[o] = xv[v] - eta * ax[fm][fn][h + v];
+            R[o] = beta * ((gv[v] + rv[v]) - ar[fm][fn][h + v]);
+          }
+        }
+      }
+}
+
 __device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
   return L.status[d.slot] != 0;
 }
@@ -266,6 +311,8 @@ __device__ __forceinline__ void epi_body(const Launch& L, const MatDesc& d, int 
     }
     __syncthreads();
   }
+  // Element by element: one batch's loads would add registers and cost this
+  // float32-MFMA-bound kernel its third wavefront per SIMD.
   gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
   gptr<float> X = to_global(d.X);
   gptr<float> R = to_global(d.R);
@@ -554,42 +601,7 @@ __device__ __forceinline__ void epi3b_body(const Launch& L, const MatDesc& d, in
                            b + 2 * CA + 3 * CB, ax, ar);
     __syncthreads();
   }
-  gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
-  gptr<float> X = to_global(d.X);
-  gptr<float> R = to_global(d.R);
-  const float eta = L.eta, beta = L.beta;
-  // Eight elements of a 32 x 32 block at a time: every load of a batch is
-  // issued before its first store (X, G and R may alias as far as the
-  // compiler knows, so loads interleaved with stores would run one element
-  // at a time).  m n < 2^31 (checked at the boundary): offsets are 32-bit.
-#pragma unroll
-  for (int fm = 0; fm < WE::FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < WE::FN; ++fn)
-#pragma unroll
-      for (int h = 0; h < 16; h += 8) {
-        const int col = tn * WE::BN + WE::col(fn);
-        float gv[8], rv[8], xv[8];
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const int row = tm * WE::BM + WE::row(fm, h + v);
-          if (FULL || (row < d.m && col < d.n)) {
-            const unsigned o = static_cast<unsigned>(row * d.n + col);
-            if constexpr (sizeof(GT) == 2) gv[v] = bf16_to_f32(G[o]); else gv[v] = G[o];
-            rv[v] = R[o];
-            xv[v] = X[o];
-          }
-        }
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const int row = tm * WE::BM + WE::row(fm, h + v);
-          if (FULL || (row < d.m && col < d.n)) {
-            const unsigned o = static_cast<unsigned>(row * d.n + col);
-            X[o] = xv[v] - eta * ax[fm][fn][h + v];
-            R[o] = beta * ((gv[v] + rv[v]) - ar[fm][fn][h + v]);
-          }
-        }
-      }
+  update_epilogue<WE, GT, FULL>(L, d, tm * WE::BM, tn * WE::BN, ax, ar);
 }
 
 template <typename GT, bool VEC>
@@ -664,28 +676,7 @@ __device__ __forceinline__ void epi3_body(const Launch& L, const MatDesc& d, int
     __syncthreads();
   }
   if (nk & 1) compute(0);
-  gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
-  gptr<float> X = to_global(d.X);
-  gptr<float> R = to_global(d.R);
-  const float eta = L.eta, beta = L.beta;
-#pragma unroll
-  for (int fm = 0; fm < Wp::FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < Wp::FN; ++fn) {
-      const int col = tn * BN + acc_col<BM, BN>(fn);
-      if (!FULL && col >= d.n) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = tm * BM + acc_row<BM, BN>(fm, v);
-        if (!FULL && row >= d.m) continue;
-        const int64_t o = static_cast<int64_t>(row) * d.n + col;
-        float g;
-        if constexpr (sizeof(GT) == 2) g = bf16_to_f32(G[o]); else g = G[o];
-        const float mv = g + R[o];
-        X[o] = X[o] - eta * ax[fm][fn][v];
-        R[o] = beta * (mv - ar[fm][fn][v]);
-      }
-    }
+  update_epilogue<WGrid<BM, BN, 2, 2>, GT, FULL>(L, d, tm * BM, tn * BN, ax, ar);
 }
 
 template <typename GT, int BN, bool VEC>
