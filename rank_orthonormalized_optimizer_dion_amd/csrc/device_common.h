@@ -195,11 +195,16 @@ struct SrcF64 {
 // cell[2q + l/32][x0 + l%32], i.e. 4 reduction steps at once; the MFMA loop
 // then pairs lanes 0-31 (k = 8q + c) with lanes 32-63 (k = 8q + 4 + c).
 // Both operands use the same k order, so the product is unchanged.
+// Row padding 32 / BK and the row swizzle tile_swz make every store pattern
+// (k-contiguous: 8 lanes on 8 rows of one x; x-contiguous: 8 lanes on x
+// 4 apart) and every MFMA read (8 lanes on consecutive x of one row) touch
+// 8 different 16-byte bank groups of the 32-bank LDS.
 template <int BX, int BK> struct TileShape {
-  static constexpr int PAD = 64 / BK;          // conflict-free cell stores
+  static constexpr int PAD = 32 / BK;
   static constexpr int PITCH = BX + PAD;       // float4 cells per kg row
   static constexpr int CELLS = (BK / 4) * PITCH;
 };
+__device__ __forceinline__ int tile_swz(int x) { return x ^ ((x >> 3) & 3); }
 
 // ---------------------------------------------------------------------------
 // Split-bfloat16 tiles (float32 products as three bfloat16 MFMA products).
@@ -398,7 +403,7 @@ struct LoadKC {
 #pragma unroll
         for (int c = 0; c < 4; ++c) val[c] = gk + c <= gx ? val[c] : 0.0f;
       }
-      lds[kq * TileShape<BX, BK>::PITCH + x] = val;
+      lds[kq * TileShape<BX, BK>::PITCH + tile_swz(x)] = val;
     }
   }
   // Split-bfloat16 store (see BfShape): each quad of 4 consecutive k is a
@@ -474,7 +479,7 @@ struct LoadXC {
         t[1] = w[1][c];
         t[2] = w[2][c];
         t[3] = w[3][c];
-        lds[kg * TileShape<BX, BK>::PITCH + 4 * xq + c] = t;
+        lds[kg * TileShape<BX, BK>::PITCH + tile_swz(4 * xq + c)] = t;
       }
     }
   }
@@ -522,10 +527,10 @@ __device__ __forceinline__ void mma_tile(const f32x4* sA, const f32x4* sB,
     f32x4 a[W::FM], b[W::FN];
 #pragma unroll
     for (int fm = 0; fm < W::FM; ++fm)
-      a[fm] = sA[(2 * q + h) * TileShape<BM, BK>::PITCH + wm * W::TM + fm * 32 + i];
+      a[fm] = sA[(2 * q + h) * TileShape<BM, BK>::PITCH + tile_swz(wm * W::TM + fm * 32 + i)];
 #pragma unroll
     for (int fn = 0; fn < W::FN; ++fn)
-      b[fn] = sB[(2 * q + h) * TileShape<BN, BK>::PITCH + wn * W::TN + fn * 32 + i];
+      b[fn] = sB[(2 * q + h) * TileShape<BN, BK>::PITCH + tile_swz(wn * W::TN + fn * 32 + i)];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -884,8 +889,8 @@ __device__ __forceinline__ void mma_tile_f64(const f32x4* sA, const f32x4* sB,
     f32x4 a[FB], b[FB];
 #pragma unroll
     for (int f = 0; f < FB; ++f) {
-      a[f] = sA[(4 * q + grp) * TileShape<BG, BK>::PITCH + wm * WT + f * 16 + i];
-      b[f] = sB[(4 * q + grp) * TileShape<BG, BK>::PITCH + wn * WT + f * 16 + i];
+      a[f] = sA[(4 * q + grp) * TileShape<BG, BK>::PITCH + tile_swz(wm * WT + f * 16 + i)];
+      b[f] = sB[(4 * q + grp) * TileShape<BG, BK>::PITCH + tile_swz(wn * WT + f * 16 + i)];
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
