@@ -144,6 +144,51 @@ def time_plan(dion, torch, mats, variant, steps, warmup, eta, beta, math="f32"):
     return (t1 - t0) / steps, {k: v / n for k, v in phases.items()}
 
 
+def time_sharded(dion, torch, whole, shards, variant, steps, warmup, eta, beta, math):
+    """Seconds per step of a DION_SHARDED plan over `shards` (one GPU's row
+    shards of the matrices `whole`), run as its three stages.  The two
+    exchanges deliver what an all-reduce over all shards would: the global
+    Gram matrix and W, taken once from stages 0 and 1 on the whole matrices
+    (which do not touch X, R or V) and copied into every shard's buffers
+    inside the timed step."""
+    full = dion.Plan(whole, variant, math=math, sharded=True)
+    wsf = full.new_workspace()
+    full.shard_stage(0, eta, beta, wsf)
+    gram = [full.shard_buffer(wsf, dion.SHARD_GRAM, i).clone() for i in range(full.count)]
+    full.shard_stage(1, eta, beta, wsf)
+    wsum = [full.shard_buffer(wsf, dion.SHARD_W, i).clone() for i in range(full.count)]
+    full.close()
+    del wsf
+    plan = dion.Plan(shards, variant, math=math, sharded=True)
+    ws = plan.new_workspace()
+    gbuf = [plan.shard_buffer(ws, dion.SHARD_GRAM, i) for i in range(plan.count)]
+    wbuf = [plan.shard_buffer(ws, dion.SHARD_W, i) for i in range(plan.count)]
+
+    def one():
+        plan.shard_stage(0, eta, beta, ws)
+        for dst, src in zip(gbuf, gram):
+            dst.copy_(src)
+        plan.shard_stage(1, eta, beta, ws)
+        for dst, src in zip(wbuf, wsum):
+            dst.copy_(src)
+        plan.shard_stage(2, eta, beta, ws)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rc, per = dion.status(ws, plan.count)
+    plan.close()
+    del ws
+    if rc != 0:
+        raise RuntimeError(f"breakdown during the sharded benchmark: {per}")
+    return (t1 - t0) / steps
+
+
 def roofline_of(phase: str, ms: float, f: dict, b: dict, traffic, math: str):
     """Roofline of one phase (one kernel launch on the 3B stack).
 
@@ -306,6 +351,17 @@ def main(argv=None) -> int:
                               wl.beta, args.math)
         extra[f"{other}_r1/{args.rank_div}"] = {"steps_per_s": round(1 / sec2, 4),
                                                 "phase_ms": {k: round(v, 3) for k, v in ph2.items()}}
+        # one GPU's share of an 8-way row-sharded (FSDP) stack: rows
+        # [0, m/8) of every matrix, stepped in the three DION_SHARDED stages
+        whole = [(d.X, d.G, d.R, d.V) for d in mats]
+        shard = [(d.X[: d.X.shape[0] // 8], d.G[: d.G.shape[0] // 8], d.R[: d.R.shape[0] // 8],
+                  d.V) for d in mats]
+        sec4 = time_sharded(dion, torch, whole, shard, args.variant, max(3, args.steps // 2), 1,
+                            wl.eta, wl.beta, args.math)
+        extra[f"{args.variant}_r1/{args.rank_div}_shard1of8"] = {
+            "steps_per_s": round(1 / sec4, 4), "rows": "m/8 of every matrix",
+            "exchange": "the all-reduced Gram matrix and W landed by device copies"}
+        del shard
         div2 = 16 if args.rank_div == 4 else 4
         wl2 = config(4, div2, layers=args.layers)
         for d, s in zip(mats, wl2.mats):

@@ -82,6 +82,43 @@ extern "C" {
 #define DION_MATH_BF16X3  0x100
 #define DION_MATH_MASK    0x100
 
+/* Row-sharded step (FSDP layout; the sharded setting the Dion and
+ * Orth-Dion abstracts motivate).  OR DION_SHARDED into the variant of
+ * dion_plan_create for a plan whose matrices are the local row shards of
+ * the global matrices: matrix i is rows [a_i, a_i + m_i) of some global
+ * X, G, R (m_i x n), and every shard of one global matrix holds its own
+ * copy of the same V (n x r).  dion_plan_shard_stage then runs the step in
+ * three stages; between them the caller sums one exchange buffer over all
+ * shards of each global matrix (an all-reduce across GPUs; with a single
+ * shard there is nothing to do) and writes the sum back into every shard's
+ * buffer:
+ *   stage 0: P_i = M_i V and the local Gram partial P_i^T P_i
+ *            -> exchange DION_SHARD_GRAM: float64, rp x rp row-major
+ *               (rp = r rounded up to 64); stage 1 reads only the upper
+ *               triangle of its leading r x r block
+ *   stage 1: T from the summed Gram matrix, U_i = P_i T^{-1},
+ *            W_i = M_i^T U_i
+ *            -> exchange DION_SHARD_W: float32, n x r row-major
+ *   stage 2: Vbar from the summed W (computed identically on every shard),
+ *            X_i and R_i updated, Vbar written into the shard's V.
+ * Summed this way the shards' results equal one step on the global
+ * matrices.  dion_plan_shard_buffer gives the byte offset (from the
+ * workspace base) and size of exchange buffer `which` (DION_SHARD_*) of
+ * matrix `index` (position in the plan's list).  Stage calls follow the
+ * order 0, 1, 2 on one workspace and stream; the buffers are valid from
+ * the end of the stage that writes them to the start of the next stage.
+ * dion_plan_step also runs a sharded plan: all three stages without
+ * exchange, i.e. each shard as a matrix of its own.  dion_step and
+ * dion_step_batched reject DION_SHARDED (DION_ERR_INVALID_ARG).  Errors:
+ * DION_ERR_INVALID_ARG for a null plan, a plan created without
+ * DION_SHARDED, a stage outside 0..2, which outside DION_SHARD_*, an index
+ * outside the list or a null output pointer; otherwise as dion_plan_step.
+ * A shard may have fewer rows than r (only r <= n is required of it); the
+ * global matrix needs at least r rows for its Gram matrix to be definite. */
+#define DION_SHARDED      0x200
+#define DION_SHARD_GRAM   0
+#define DION_SHARD_W      1
+
 /* Element type of G. */
 #define DION_DTYPE_F32  0
 #define DION_DTYPE_BF16 1
@@ -156,6 +193,11 @@ int    dion_plan_count(const dion_plan* plan);
 int    dion_plan_step(dion_plan* plan, float eta, float beta,
                       void* workspace, size_t workspace_bytes, void* stream);
 void   dion_plan_destroy(dion_plan* plan);
+
+int dion_plan_shard_stage(dion_plan* plan, int stage, float eta, float beta,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int dion_plan_shard_buffer(const dion_plan* plan, int which, int index,
+                           size_t* offset, size_t* bytes);
 
 /* Phase timing, for measurement.  A step runs five phases, in order:
  *   0  P = M V            1  U = orth(P)          2  W = M^T U

@@ -30,6 +30,8 @@ ERR_BREAKDOWN = -4
 
 VARIANTS = {"dion": 0, "orth": 1}
 MATH = {"f32": 0x000, "bf16x3": 0x100}
+SHARDED = 0x200
+SHARD_GRAM, SHARD_W = 0, 1
 STATUS_ORTH_P, STATUS_ORTH_W, STATUS_COLNORM = 1, 2, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +93,9 @@ def load() -> ctypes.CDLL:
         "dion_plan_timing_enable": (c_int, [vp, c_int]),
         "dion_plan_timing_read": (c_int, [vp, ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(c_int)]),
+        "dion_plan_shard_stage": (c_int, [vp, c_int, c_f, c_f, vp, c_size, vp]),
+        "dion_plan_shard_buffer": (c_int, [vp, c_int, c_int, ctypes.POINTER(c_size),
+                                           ctypes.POINTER(c_size)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -247,15 +252,17 @@ def step_batched(mats: Sequence[Tuple], eta: float, beta: float, variant="orth",
 class Plan:
     """A grouped step over a fixed list of matrices (dion_plan_*)."""
 
-    def __init__(self, mats: Sequence[Tuple], variant="orth", math="f32"):
+    def __init__(self, mats: Sequence[Tuple], variant="orth", math="f32", sharded=False):
+        """sharded: the matrices are row shards of global matrices, stepped
+        with dion_plan_shard_stage / shard_buffer (see include/dion.h)."""
         arr, gd = _mat_array(mats)
         self._lib = load()
         self._mats = list(mats)          # keep the tensors alive
         self.count = len(mats)
         self.device = mats[0][0].device
         h = ctypes.c_void_p()
-        rc = self._lib.dion_plan_create(arr, self.count, _variant(variant, math), gd,
-                                        ctypes.byref(h))
+        var = _variant(variant, math) | (SHARDED if sharded else 0)
+        rc = self._lib.dion_plan_create(arr, self.count, var, gd, ctypes.byref(h))
         if rc != OK:
             raise _err(rc)
         self._h = h
@@ -273,6 +280,34 @@ class Plan:
                                       self.workspace_bytes, _stream_handle(stream, self.device))
         if rc != OK:
             raise _err(rc)
+
+    def shard_stage(self, stage: int, eta: float, beta: float, workspace, stream=None):
+        """Stage 0, 1 or 2 of a sharded step (dion_plan_shard_stage)."""
+        if self._h is None:
+            raise RuntimeError("plan is closed")
+        if workspace.numel() * workspace.element_size() < self.workspace_bytes:
+            raise ValueError("workspace too small")
+        rc = self._lib.dion_plan_shard_stage(self._h, int(stage), float(eta), float(beta),
+                                             workspace.data_ptr(), self.workspace_bytes,
+                                             _stream_handle(stream, self.device))
+        if rc != OK:
+            raise _err(rc)
+
+    def shard_buffer(self, workspace, which: int, index: int):
+        """The exchange buffer `which` (SHARD_GRAM: float64 rp x rp; SHARD_W:
+        float32 n x r) of matrix `index`, as a view into `workspace`."""
+        torch = _torch()
+        off, nbytes = ctypes.c_size_t(), ctypes.c_size_t()
+        rc = self._lib.dion_plan_shard_buffer(self._h, int(which), int(index), ctypes.byref(off),
+                                              ctypes.byref(nbytes))
+        if rc != OK:
+            raise _err(rc)
+        raw = workspace.view(torch.uint8)[off.value:off.value + nbytes.value]
+        if which == SHARD_GRAM:
+            rp = int(round((nbytes.value // 8) ** 0.5))
+            return raw.view(torch.float64).view(rp, rp)
+        n, r = self._mats[index][3].shape
+        return raw.view(torch.float32).view(n, r)
 
     PHASES = ("mv", "orth_p", "mtu", "right", "update")
 

@@ -64,6 +64,7 @@ struct ClassRec {
 struct dion_plan {
   int count = 0, variant = 0, gdtype = 0;
   int math = 0;                       // 0: float32 MFMA, 1: split-bfloat16
+  bool sharded = false;               // DION_SHARDED: staged step with exchanges
   bool vec = false;
   bool single = false;
   std::vector<dion::ClassRec> cls;
@@ -86,11 +87,14 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-int validate_matrix(const dion_matrix& a, int gdtype) {
+// sharded: a row shard of a larger matrix, whose rows may be fewer than r
+// (the summed Gram matrix has the global row count).
+int validate_matrix(const dion_matrix& a, int gdtype, bool sharded) {
   if (!a.X || !a.G || !a.R || !a.V) return DION_ERR_INVALID_ARG;
   if (a.m < 1 || a.n < 1 || a.m > DION_MAX_DIM || a.n > DION_MAX_DIM) return DION_ERR_INVALID_ARG;
   if (a.m * a.n > INT32_MAX) return DION_ERR_INVALID_ARG;
-  if (a.r < 1 || a.r > std::min(a.m, a.n) || a.r > DION_MAX_RANK) return DION_ERR_INVALID_ARG;
+  if (a.r < 1 || a.r > (sharded ? a.n : std::min(a.m, a.n)) || a.r > DION_MAX_RANK)
+    return DION_ERR_INVALID_ARG;
   const size_t eg = gdtype == DION_DTYPE_BF16 ? 2 : 4;
   auto misaligned = [](const void* p, size_t al) { return reinterpret_cast<uintptr_t>(p) % al != 0; };
   if (misaligned(a.X, 4) || misaligned(a.R, 4) || misaligned(a.V, 4) || misaligned(a.G, eg))
@@ -126,18 +130,20 @@ void pick_split(int64_t tiles, int K, int& s, int& klen) {
 int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool single,
                dion_plan& p) {
   if (!mats || count < 1) return DION_ERR_INVALID_ARG;
-  if (variant & ~(DION_VARIANT_MASK | DION_MATH_MASK)) return DION_ERR_INVALID_ARG;
+  if (variant & ~(DION_VARIANT_MASK | DION_MATH_MASK | DION_SHARDED)) return DION_ERR_INVALID_ARG;
+  if ((variant & DION_SHARDED) && single) return DION_ERR_INVALID_ARG;
   const int rule = variant & DION_VARIANT_MASK;
   if (rule != DION_VARIANT_DION && rule != DION_VARIANT_ORTH) return DION_ERR_INVALID_ARG;
   if (gdtype != DION_DTYPE_F32 && gdtype != DION_DTYPE_BF16) return DION_ERR_INVALID_ARG;
   p.count = count;
   p.variant = rule;
   p.math = (variant & DION_MATH_BF16X3) ? 1 : 0;
+  p.sharded = (variant & DION_SHARDED) != 0;
   p.gdtype = gdtype;
   p.single = single;
   p.vec = true;
   for (int i = 0; i < count; ++i) {
-    const int rc = validate_matrix(mats[i], gdtype);
+    const int rc = validate_matrix(mats[i], gdtype, p.sharded);
     if (rc != DION_OK) return rc;
     p.vec = p.vec && vec_ok(mats[i], gdtype);
   }
@@ -186,6 +192,10 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     pick_split(t_mv, k.n, k.s_mv, k.kl_mv);
     pick_split(t_mtu, k.m, k.s_mtu, k.kl_mtu);
     pick_split(t_gp, k.m, k.s_gp, k.kl_gp);
+    if (p.sharded) {   // the Gram exchange buffer is one plane of S
+      k.s_gp = 1;
+      k.kl_gp = cdiv(k.m, kBK) * kBK;
+    }
     pick_split(t_gw, k.n, k.s_gw, k.kl_gw);
   }
   // Workspace: status words | matrix table (grouped calls) | per-matrix buffers.
@@ -274,12 +284,11 @@ hipError_t grouped(const dion_plan& p, const Launch& base, Fill fill, Go go) {
 // orth() of the P (which = 0) or W (which = 1) factor by one CholeskyQR
 // pass with a float64 Gram matrix: S = Q^T Q (float64 MFMA), S = T^T T and
 // Y = T^{-T} (float64, blocked), Q T^{-1} (float32 MFMA) into U (oB) or V.
-hipError_t orth(const dion_plan& p, Launch base, int which, hipStream_t st) {
+// gram() writes the Gram partials into oS; factor() does the rest.
+hipError_t gram(const dion_plan& p, Launch base, int which, hipStream_t st) {
   base.which = which;
   base.pass = 1;
   base.flag = which == 0 ? DION_STATUS_ORTH_P : DION_STATUS_ORTH_W;
-  int max_nblk = 0;
-  for (const ClassRec& c : p.cls) max_nblk = std::max(max_nblk, c.rp / kCholNB);
   for (int bg : {128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bg != bg) return false;
@@ -291,6 +300,15 @@ hipError_t orth(const dion_plan& p, Launch base, int which, hipStream_t st) {
       return true;
     }, [&](const Launch& L) { return launch_gram(L, bg, p.vec, st); }));
   }
+  return hipSuccess;
+}
+
+hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
+  base.which = which;
+  base.pass = 1;
+  base.flag = which == 0 ? DION_STATUS_ORTH_P : DION_STATUS_ORTH_W;
+  int max_nblk = 0;
+  for (const ClassRec& c : p.cls) max_nblk = std::max(max_nblk, c.rp / kCholNB);
   DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
     const int nb = c.rp / kCholNB;
     ci.splits = which == 0 ? c.s_gp : c.s_gw;
@@ -345,8 +363,11 @@ struct Marker {
   }
 };
 
+// Stages first..last of the step (the stages of DION_SHARDED; 0..2 is the
+// whole step): 0 = P and its Gram partials, 1 = U and W, 2 = Vbar, X, R.
 hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, float beta,
-                    char* ws, hipStream_t st, const Marker& mk = Marker{}) {
+                    char* ws, hipStream_t st, const Marker& mk = Marker{}, int first = 0,
+                    int last = 2) {
   Launch base{};
   base.table = dev_table;
   if (p.single) base.inl = p.table[0];
@@ -356,6 +377,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   base.beta = beta;
   const int ept = elems_per_tile();
 
+  if (first <= 0 && last >= 0) {
   // P = M V (split-bfloat16: V^T split once into planes, read as whole cells
   // by every tile)
   DION_TRY(mk.mark(0, st));
@@ -379,9 +401,13 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
     return true;
   }, [&](const Launch& L) { return launch_reduce(L, st); }));
 
-  // U = orth(P)
+  // U = orth(P): the Gram partials here, the rest in stage 1
   DION_TRY(mk.mark(1, st));
-  DION_TRY(orth(p, base, 0, st));
+  DION_TRY(gram(p, base, 0, st));
+  }
+
+  if (first <= 1 && last >= 1) {
+  DION_TRY(factor(p, base, 0, st));
   DION_TRY(mk.mark(2, st));
 
   // W = M^T U (split-bfloat16: U^T split once into planes, read as whole
@@ -406,10 +432,14 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
     return true;
   }, [&](const Launch& L) { return launch_reduce(L, st); }));
 
+  }
+
+  if (first <= 2 && last >= 2) {
   // Vbar into V
   DION_TRY(mk.mark(3, st));
   if (p.variant == DION_VARIANT_ORTH) {
-    DION_TRY(orth(p, base, 1, st));
+    DION_TRY(gram(p, base, 1, st));
+    DION_TRY(factor(p, base, 1, st));
   } else {
     base.flag = DION_STATUS_COLNORM;
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
@@ -440,6 +470,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
     }, [&](const Launch& L) { return launch_epi(L, p.gdtype, bn, p.vec, p.math, st); }));
   }
   DION_TRY(mk.mark(5, st));
+  }
   return hipSuccess;
 }
 
@@ -484,7 +515,10 @@ int plan_alloc_host(dion_plan* p) {
   return DION_OK;
 }
 
-int plan_step(dion_plan* p, float eta, float beta, void* ws, size_t bytes, hipStream_t st) {
+// Stages first..last of a grouped step (0..2: the whole step, timed when
+// timing is enabled; a single stage: one stage of a sharded step).
+int plan_step(dion_plan* p, float eta, float beta, void* ws, size_t bytes, hipStream_t st,
+              int first = 0, int last = 2) {
   int rc = check_call(*p, eta, beta, ws, bytes);
   if (rc != DION_OK) return rc;
   char* w = static_cast<char*>(ws);
@@ -495,8 +529,10 @@ int plan_step(dion_plan* p, float eta, float beta, void* ws, size_t bytes, hipSt
   if (hipEventRecord(p->ev, st) != hipSuccess) return DION_ERR_HIP;
   p->ev_pending = true;
   Marker mk;
-  if (p->t_count < p->t_max) mk.ev = &p->tev[static_cast<size_t>(p->t_count++) * (DION_PHASES + 1)];
-  return run_step(*p, dev_table, eta, beta, w, st, mk) == hipSuccess ? DION_OK : DION_ERR_HIP;
+  if (first == 0 && last == 2 && p->t_count < p->t_max)
+    mk.ev = &p->tev[static_cast<size_t>(p->t_count++) * (DION_PHASES + 1)];
+  return run_step(*p, dev_table, eta, beta, w, st, mk, first, last) == hipSuccess ? DION_OK
+                                                                                  : DION_ERR_HIP;
 }
 
 // Cache of grouped plans keyed by the matrix list (most recent first).
@@ -572,6 +608,7 @@ DION_API int dion_step(float* X, const void* G, float* R, float* V, int64_t m, i
 
 DION_API size_t dion_workspace_size_batched(const dion_matrix* mats, int count, int variant,
                                             int g_dtype) {
+  if (variant & DION_SHARDED) return 0;   // sharded steps run through a plan
   dion_plan p;
   if (build_plan(mats, count, variant, g_dtype, false, p) != DION_OK) return 0;
   return p.ws_bytes;
@@ -606,6 +643,32 @@ DION_API int dion_plan_step(dion_plan* plan, float eta, float beta, void* worksp
 }
 
 DION_API void dion_plan_destroy(dion_plan* plan) { plan_free(plan); }
+
+DION_API int dion_plan_shard_stage(dion_plan* plan, int stage, float eta, float beta,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !plan->sharded || stage < 0 || stage > 2) return DION_ERR_INVALID_ARG;
+  return plan_step(plan, eta, beta, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                   stage, stage);
+}
+
+DION_API int dion_plan_shard_buffer(const dion_plan* plan, int which, int index, size_t* offset,
+                                    size_t* bytes) {
+  if (!plan || !plan->sharded || !offset || !bytes) return DION_ERR_INVALID_ARG;
+  if (which != DION_SHARD_GRAM && which != DION_SHARD_W) return DION_ERR_INVALID_ARG;
+  if (index < 0 || index >= plan->count) return DION_ERR_INVALID_ARG;
+  for (const MatDesc& d : plan->table) {
+    if (d.slot != index) continue;
+    if (which == DION_SHARD_GRAM) {
+      *offset = static_cast<size_t>(d.oS);
+      *bytes = static_cast<size_t>(d.rp) * d.rp * 8;
+    } else {
+      *offset = static_cast<size_t>(d.oW);
+      *bytes = static_cast<size_t>(d.n) * d.r * 4;
+    }
+    return DION_OK;
+  }
+  return DION_ERR_INVALID_ARG;
+}
 
 DION_API int dion_plan_timing_enable(dion_plan* plan, int max_steps) {
   if (!plan || max_steps < 0 || max_steps > (1 << 20)) return DION_ERR_INVALID_ARG;
@@ -654,7 +717,7 @@ DION_API int dion_plan_timing_read(dion_plan* plan, double* ms_per_phase, int* s
 DION_API int dion_step_batched(const dion_matrix* mats, int count, float eta, float beta,
                                int variant, int g_dtype, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  if (!mats || count < 1) return DION_ERR_INVALID_ARG;
+  if (!mats || count < 1 || (variant & DION_SHARDED)) return DION_ERR_INVALID_ARG;
   std::vector<uint64_t> key = make_key(mats, count, variant, g_dtype);
   std::lock_guard<std::mutex> lock(g_cache_mu);
   dion_plan* hit = nullptr;

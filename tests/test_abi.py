@@ -106,3 +106,21 @@ def test_batched_validation(lib):
     assert lib.dion_plan_create(mats, 2, 5, 0, ctypes.byref(h)) == dion.ERR_INVALID_ARG
     assert not h.value
     assert lib.dion_status(None, 1, None, None) == dion.ERR_INVALID_ARG
+
+
+def test_sharded_variant_rejected_outside_plans(lib):
+    sharded = 1 | 0x200
+    assert step(lib, variant=sharded, nbytes=1 << 30) == dion.ERR_INVALID_ARG
+    assert lib.dion_workspace_size(64, 32, 8, sharded, 0) == 0
+    mats = (dion.dion_matrix * 1)(dion.dion_matrix(FX, FG, FR, FV, 64, 32, 8))
+    assert lib.dion_workspace_size_batched(mats, 1, sharded, 0) == 0
+    assert lib.dion_step_batched(mats, 1, 0.01, 0.95, sharded, 0, FW, 1 << 30, None) == \
+        dion.ERR_INVALID_ARG
+
+
+def test_shard_entry_points_reject_null_plan(lib):
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.dion_plan_shard_stage(None, 0, 0.01, 0.95, FW, 1 << 30, None) == \
+        dion.ERR_INVALID_ARG
+    assert lib.dion_plan_shard_buffer(None, 0, 0, ctypes.byref(off), ctypes.byref(nb)) == \
+        dion.ERR_INVALID_ARG
