@@ -302,6 +302,40 @@ struct LoadDma {
   }
 };
 
+// Three-way split for float32-accurate products on the bfloat16 matrix
+// cores: x = hi + mid + lo with hi = bf16(x), mid = bf16(x - hi),
+// lo = bf16(x - hi - mid) (both differences exact), 24 significant bits in
+// all.  A product keeps the six terms of weight >= 2^-16 (hh, hm, mh, hl,
+// lh, mm); the dropped ones are below 3 2^-24 |a b|, the order of float32
+// rounding itself.
+__device__ __forceinline__ void bf_split4x3(const f32x4& v, u32x2& hi, u32x2& mid, u32x2& lo) {
+  u32x2 h, rest;
+  bf_split4(v, h, rest);   // rest = bf16(x - hi): that is mid
+  mid = rest;
+  f32x4 r;
+  r[0] = v[0] - __uint_as_float(h.x << 16) - __uint_as_float(mid.x << 16);
+  r[1] = v[1] - __uint_as_float(h.x & 0xffff0000u) - __uint_as_float(mid.x & 0xffff0000u);
+  r[2] = v[2] - __uint_as_float(h.y << 16) - __uint_as_float(mid.y << 16);
+  r[3] = v[3] - __uint_as_float(h.y & 0xffff0000u) - __uint_as_float(mid.y & 0xffff0000u);
+  const bf16x2 l01 = {static_cast<__bf16>(r[0]), static_cast<__bf16>(r[1])};
+  const bf16x2 l23 = {static_cast<__bf16>(r[2]), static_cast<__bf16>(r[3])};
+  hi = h;
+  lo.x = __builtin_bit_cast(unsigned, l01);
+  lo.y = __builtin_bit_cast(unsigned, l23);
+}
+
+// bf_store_quad for the three planes of bf_split4x3.
+template <int BX>
+__device__ __forceinline__ void bf_store_quad3(u32x2* hi, u32x2* mid, u32x2* lo, int kq, int x,
+                                               const f32x4& v) {
+  u32x2 h, m, l;
+  bf_split4x3(v, h, m, l);
+  const int slot = ((kq >> 1) * (BX + 4) + bf_swz(x)) * 2 + (kq & 1);
+  hi[slot] = h;
+  mid[slot] = m;
+  lo[slot] = l;
+}
+
 // Loader of split-bfloat16 planes written ahead of time (hi and lo, zero
 // past the reduction length) in the K-blocked cell order of plane_cell():
 // the BK = kPlaneK slice of BX consecutive rows is one contiguous run of
@@ -404,6 +438,21 @@ struct LoadKC {
         for (int c = 0; c < 4; ++c) val[c] = gk + c <= gx ? val[c] : 0.0f;
       }
       lds[kq * TileShape<BX, BK>::PITCH + tile_swz(x)] = val;
+    }
+  }
+  // Three-plane store of bf_split4x3 (hi, mid, lo), otherwise as store_bf.
+  __device__ __forceinline__ void store_bf3(u32x2* hi, u32x2* mid, u32x2* lo) const {
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      const int idx = threadIdx.x + NT * s;
+      const int kq = idx % KQ, x = idx / KQ;
+      f32x4 val = Src::fin(v[s]);
+      if constexpr (TRI) {
+        const int gx = x0 + x, gk = kcur + 4 * kq;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) val[c] = gk + c <= gx ? val[c] : 0.0f;
+      }
+      bf_store_quad3<BX>(hi, mid, lo, kq, x, val);
     }
   }
   // Split-bfloat16 store (see BfShape): each quad of 4 consecutive k is a
@@ -773,6 +822,47 @@ __device__ __forceinline__ void mma_tile_bf3w2(const u32x4* ah, const u32x4* al,
         ac[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], c_lo[fn], ac[fm][fn], 0, 0, 0);
         ab[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], b_hi[fn], ab[fm][fn], 0, 0, 0);
         ac[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[fm], c_hi[fn], ac[fm][fn], 0, 0, 0);
+      }
+  }
+}
+
+// Float32-accurate product tile from three-way split operands: the six
+// terms hh, hm, mh, hl, lh, mm of bf_split4x3 per 16 k.  Planes: A hi, mid,
+// lo at ah, ah + CA, ah + 2 CA; B likewise from bh with stride CB.
+template <int BM, int BN, int BK>
+__device__ __forceinline__ void mma_tile_bf6(const u32x4* ah, const u32x4* bh,
+                                             f32x16 (&acc)[Warps<BM, BN>::FM][Warps<BM, BN>::FN]) {
+  using W = Warps<BM, BN>;
+  constexpr int CA = BfShape<BM, BK>::CELLS, CB = BfShape<BN, BK>::CELLS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, i = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int q = 0; q < BK / 16; ++q) {
+    bf16x8 a[3][W::FM], b[3][W::FN];
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm) {
+      const int c = (2 * q + h) * BfShape<BM, BK>::PITCH + bf_swz(wm * W::TM + fm * 32 + i);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) a[p][fm] = __builtin_bit_cast(bf16x8, ah[p * CA + c]);
+    }
+#pragma unroll
+    for (int fn = 0; fn < W::FN; ++fn) {
+      const int c = (2 * q + h) * BfShape<BN, BK>::PITCH + bf_swz(wn * W::TN + fn * 32 + i);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) b[p][fn] = __builtin_bit_cast(bf16x8, bh[p * CB + c]);
+    }
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < W::FN; ++fn) {
+        f32x16 t = acc[fm][fn];
+        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][fm], b[1][fn], t, 0, 0, 0);   // mm
+        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2][fm], b[0][fn], t, 0, 0, 0);   // lh
+        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][fm], b[2][fn], t, 0, 0, 0);   // hl
+        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][fm], b[0][fn], t, 0, 0, 0);   // mh
+        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][fm], b[1][fn], t, 0, 0, 0);   // hm
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][fm], b[0][fn], t, 0, 0, 0);
       }
   }
 }

@@ -339,7 +339,7 @@ hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
       ci.ty = cdiv(c.r, bn);
       ci.tiles = ci.tx * ci.ty;
       return true;
-    }, [&](const Launch& L) { return launch_trmm(L, bn, p.vec, st); }));
+    }, [&](const Launch& L) { return launch_trmm(L, bn, p.vec, p.math, st); }));
   }
   return hipSuccess;
 }

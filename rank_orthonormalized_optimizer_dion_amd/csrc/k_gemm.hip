@@ -3,7 +3,8 @@
 //   k_mv    P = M V            (M = G + R formed while loading)
 //   k_mtu   W = M^T U          (equation 3)
 //   k_gram  S = Q^T Q          (Gram matrix of a CholeskyQR pass)
-//   k_trmm  Q' = Q T^{-1}      (T^{-1} upper triangular, read from T^{-T})
+//   k_trmm  Q' = Q T^{-1}      (T^{-1} upper triangular, read from T^{-T});
+//           k_trmm6 the same with float32 accuracy on bfloat16 matrix cores
 //   k_epi   X -= eta U Vbar^T and R = beta (M - U W^T)   (equations 5, 6)
 #include "device_common.h"
 #include "launchers.h"
@@ -265,6 +266,66 @@ __global__ __launch_bounds__(kThreads) void k_trmm(Launch L) {
   const bool full = VEC && (tm + 1) * BM <= rows && (tn + 1) * BN <= d.r && kend % BK == 0;
   if (full) trmm_body<BN, VEC, true>(L, d, rows, tm, tn, kend, smem);
   else trmm_body<BN, VEC, false>(L, d, rows, tm, tn, kend, smem);
+}
+
+// Q T^{-1} with float32 accuracy on the bfloat16 matrix cores (split-
+// bfloat16 plans): both operands split three ways (bf_split4x3), six
+// bfloat16 products per float32 product, float32 accumulation.  BK = 16 so
+// that two stages of three planes per operand leave room for three blocks
+// per CU.
+template <int BN, bool VEC, bool FULL>
+__device__ __forceinline__ void trmm6_body(const Launch& L, const MatDesc& d, int rows, int tm,
+                                           int tn, int kend, u32x4* smem) {
+  constexpr int BK = 16;
+  constexpr int CA = BfShape<BM, BK>::CELLS, CB = BfShape<BN, BK>::CELLS;
+  constexpr int STAGE = 3 * (CA + CB);
+  const float* Q = qr_source(L, d);
+  float* dst = L.which == 0 ? reinterpret_cast<float*>(L.ws + d.oB) : d.V;
+  const double* Y = reinterpret_cast<const double*>(L.ws + d.oY);
+  LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{Q}, d.r, tm * BM, rows, kend);
+  LoadKC<BN, BK, true, true, SrcF64> lb(SrcF64{Y}, d.rp, tn * BN, d.r, kend);
+  f32x16 acc[Warps<BM, BN>::FM][Warps<BM, BN>::FN];
+  zero_acc(acc);
+  auto store = [&](int st) {
+    u32x2* b = reinterpret_cast<u32x2*>(smem + st * STAGE);
+    la.store_bf3(b, b + 2 * CA, b + 4 * CA);
+    lb.store_bf3(b + 6 * CA, b + 6 * CA + 2 * CB, b + 6 * CA + 4 * CB);
+  };
+  const int nk = (kend + BK - 1) / BK;
+  la.template load<FULL>(0);
+  lb.template load<FULL>(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.template load<FULL>((kt + 1) * BK);
+      lb.template load<FULL>((kt + 1) * BK);
+    }
+    const u32x4* b = smem + (kt & 1) * STAGE;
+    mma_tile_bf6<BM, BN, BK>(b, b + 3 * CA, acc);
+    if (more) store((kt + 1) & 1);
+    __syncthreads();
+  }
+  store_tile<BM, BN>(dst, d.r, tm * BM, tn * BN, rows, d.r, acc);
+}
+
+template <int BN, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_trmm6(Launch L) {
+  constexpr int BK = 16;
+  __shared__ u32x4 smem[2 * 3 * (BfShape<BM, BK>::CELLS + BfShape<BN, BK>::CELLS)];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int rows = L.which == 0 ? d.m : d.n;
+  int tm, tn;
+  tile_order(local, ci.tx, ci.ty, tm, tn);
+  const int kend = min(d.r, (tn + 1) * BN);
+  const bool full = VEC && (tm + 1) * BM <= rows && (tn + 1) * BN <= d.r && kend % BK == 0;
+  if (full) trmm6_body<BN, VEC, true>(L, d, rows, tm, tn, kend, smem);
+  else trmm6_body<BN, VEC, false>(L, d, rows, tm, tn, kend, smem);
 }
 
 // Fused weight and residual update over one BM x BN tile of X and R:
@@ -741,7 +802,11 @@ hipError_t launch_gram(const Launch& L, int bg, bool vec, hipStream_t st) {
   return vec ? go(k_gram<64, true>, L, st) : go(k_gram<64, false>, L, st);
 }
 
-hipError_t launch_trmm(const Launch& L, int bn, bool vec, hipStream_t st) {
+hipError_t launch_trmm(const Launch& L, int bn, bool vec, int math, hipStream_t st) {
+  if (math) {
+    if (bn == 128) return vec ? go(k_trmm6<128, true>, L, st) : go(k_trmm6<128, false>, L, st);
+    return vec ? go(k_trmm6<64, true>, L, st) : go(k_trmm6<64, false>, L, st);
+  }
   if (bn == 128) return vec ? go(k_trmm<128, true>, L, st) : go(k_trmm<128, false>, L, st);
   return vec ? go(k_trmm<64, true>, L, st) : go(k_trmm<64, false>, L, st);
 }
