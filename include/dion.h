@@ -201,7 +201,9 @@ int dion_plan_shard_buffer(const dion_plan* plan, int which, int index,
 
 /* Phase timing, for measurement.  A step runs five phases, in order:
  *   0  P = M V            1  U = orth(P)          2  W = M^T U
- *   3  Vbar (orth(W) or column normalization)     4  X and R update
+ *   3  Vbar (orth(W) or column normalization; with split-bfloat16 products
+ *      also the bfloat16 planes of U, W and Vbar the update reads)
+ *   4  X and R update (the update kernel alone)
  * dion_plan_timing_enable(plan, max_steps) makes the next max_steps calls of
  * dion_plan_step record a HIP event at every phase boundary on the step's
  * stream (creating the events now; 0 disables and frees them).

@@ -452,14 +452,16 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
     }, [&](const Launch& L) { return launch_colscale(L, st); }));
   }
 
-  // X and R (large split-bfloat16 tiles: U, W, Vbar split into planes first)
-  DION_TRY(mk.mark(4, st));
+  // U, W and Vbar as split-bfloat16 planes for the large update tiles
   DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
     if (c.bn_n != 256) return false;
     const int cr = cdiv(c.r, kSplitTile);
     ci.tiles = (cdiv(c.m, kSplitTile) + 2 * cdiv(c.n, kSplitTile)) * cr;
     return true;
   }, [&](const Launch& L) { return launch_split_n(L, st); }));
+
+  // X and R
+  DION_TRY(mk.mark(4, st));
   for (int bn : {256, 128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_n != bn) return false;
