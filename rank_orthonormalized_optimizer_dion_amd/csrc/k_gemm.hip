@@ -37,15 +37,95 @@ __device__ __forceinline__ void store_tile(float* out_, int64_t ld, int r0, int 
 
 // The fused update's epilogue for a tile at (r0, c0) whose accumulators
 // hold U Vbar^T (ax) and U W^T (ar) in the 32 x 32 MFMA layout of wavefront
-// grid W: X -= eta ax, R = beta ((G + R) - ar).  Eight elements at a time,
-// every load of a batch issued before its first store (X, G and R may alias
-// as far as the compiler knows, so loads interleaved with stores would run
-// one element at a time).  m n < 2^31 (checked at the boundary): offsets
-// are 32-bit.
-template <class W, typename GT, bool FULL>
+// grid W: X -= eta ax, R = beta ((G + R) - ar).
+//
+// Interior tiles: the 16 values of one accumulator block sit in 4 groups of
+// 8 rows; within a group the lane's 4 rows are at fixed offsets from the
+// group's first element.  That element's address is wavefront-uniform (a
+// scalar base), so every load and store is a scalar base plus one of 4
+// per-lane 32-bit byte offsets (the group spans 8 rows: 8 n < 2^28 when
+// m >= 256 and m n < 2^31).  E elements per lane are loaded before the
+// first store of a batch (X, G and R may alias as far as the compiler
+// knows, so loads interleaved with stores would wait one element at a time).
+//
+// Edge tiles check every element, 8 at a time.  m n < 2^31 (checked at the
+// boundary): element offsets are 32-bit.
+template <class T>
+__device__ __forceinline__ gptr<T> uniform_ptr(gptr<T> p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<gptr<T>>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <class T>
+__device__ __forceinline__ gptr<T> byte_off(gptr<T> base, uint32_t bytes) {
+  return reinterpret_cast<gptr<T>>(reinterpret_cast<gptr<char>>(const_cast<gptr<char>>(
+                                       reinterpret_cast<gptr<const char>>(base))) + bytes);
+}
+
+template <class W, typename GT, int E>
+__device__ __forceinline__ void update_epilogue_full(const Launch& L, const MatDesc& d, int r0,
+                                                     int c0, const f32x16 (&ax)[W::FM][W::FN],
+                                                     const f32x16 (&ar)[W::FM][W::FN]) {
+  static_assert(E % 4 == 0, "whole groups of 4 rows");
+  constexpr int GPB = E / 4, NGRP = W::FM * W::FN * 4;
+  static_assert(NGRP % GPB == 0, "batch must divide the groups");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wm = wave / W::GN, wn = wave % W::GN;
+  const uint32_t n = static_cast<uint32_t>(d.n);
+  uint32_t o4[4], o2[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t e = (4u * static_cast<uint32_t>(lane >> 5) + j) * n + static_cast<uint32_t>(lane & 31);
+    o4[j] = 4u * e;
+    o2[j] = static_cast<uint32_t>(sizeof(GT)) * e;
+  }
+  const float eta = L.eta, beta = L.beta;
+#pragma unroll
+  for (int g0 = 0; g0 < NGRP; g0 += GPB) {
+    float gv[E], rv[E], xv[E];
+#pragma unroll
+    for (int b = 0; b < GPB; ++b) {
+      const int g = g0 + b, fm = g / (4 * W::FN), fn = (g / 4) % W::FN, q = g % 4;
+      const int64_t e0 = static_cast<int64_t>(r0 + wm * W::TM + fm * 32 + 8 * q) * d.n +
+                         (c0 + wn * W::TN + fn * 32);
+      const gptr<const GT> gp = uniform_ptr(to_global(static_cast<const GT*>(d.G)) + e0);
+      const gptr<const float> xp = uniform_ptr(to_global(static_cast<const float*>(d.X)) + e0);
+      const gptr<const float> rp = uniform_ptr(to_global(static_cast<const float*>(d.R)) + e0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(GT) == 2) gv[4 * b + j] = bf16_to_f32(*byte_off(gp, o2[j]));
+        else gv[4 * b + j] = *byte_off(gp, o2[j]);
+        rv[4 * b + j] = *byte_off(rp, o4[j]);
+        xv[4 * b + j] = *byte_off(xp, o4[j]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < GPB; ++b) {
+      const int g = g0 + b, fm = g / (4 * W::FN), fn = (g / 4) % W::FN, q = g % 4;
+      const int64_t e0 = static_cast<int64_t>(r0 + wm * W::TM + fm * 32 + 8 * q) * d.n +
+                         (c0 + wn * W::TN + fn * 32);
+      const gptr<float> xp = uniform_ptr(to_global(d.X) + e0);
+      const gptr<float> rp = uniform_ptr(to_global(d.R) + e0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *byte_off(xp, o4[j]) = xv[4 * b + j] - eta * ax[fm][fn][4 * q + j];
+        *byte_off(rp, o4[j]) = beta * ((gv[4 * b + j] + rv[4 * b + j]) - ar[fm][fn][4 * q + j]);
+      }
+    }
+  }
+}
+
+template <class W, typename GT, bool FULL, int E = 8>
 __device__ __forceinline__ void update_epilogue(const Launch& L, const MatDesc& d, int r0, int c0,
                                                 const f32x16 (&ax)[W::FM][W::FN],
                                                 const f32x16 (&ar)[W::FM][W::FN]) {
+  if constexpr (FULL) {
+    update_epilogue_full<W, GT, E>(L, d, r0, c0, ax, ar);
+    return;
+  }
   gptr<const GT> G = to_global(static_cast<const GT*>(d.G));
   gptr<float> X = to_global(d.X);
   gptr<float> R = to_global(d.R);
@@ -61,7 +141,7 @@ __device__ __forceinline__ void update_epilogue(const Launch& L, const MatDesc& 
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
           const int row = r0 + W::row(fm, h + v);
-          if (FULL || (row < d.m && col < d.n)) {
+          if (row < d.m && col < d.n) {
             const unsigned o = static_cast<unsigned>(row * d.n + col);
             if constexpr (sizeof(GT) == 2) gv[v] = bf16_to_f32(G[o]); else gv[v] = G[o];
             rv[v] = R[o];
@@ -71,7 +151,7 @@ __device__ __forceinline__ void update_epilogue(const Launch& L, const MatDesc& 
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
           const int row = r0 + W::row(fm, h + v);
-          if (FULL || (row < d.m && col < d.n)) {
+          if (row < d.m && col < d.n) {
             const unsigned o = static_cast<unsigned>(row * d.n + col);
             X[o] = xv[v] - eta * ax[fm][fn][h + v];
             R[o] = beta * ((gv[v] + rv[v]) - ar[fm][fn][h + v]);
@@ -622,6 +702,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_mtu3(Launch L) {
 // two per SIMD, each holding both products (U Vbar^T, U W^T).  The rank-r
 // factors come as split-bfloat16 planes written by k_split_n and are copied
 // straight into LDS.
+#ifndef DION_EPI_BATCH
+#define DION_EPI_BATCH 32
+#endif
+constexpr int kEpiBatch = DION_EPI_BATCH;
 using WE = WGrid<256, 128, 4, 2>;
 
 template <typename GT, bool VEC, bool FULL>
@@ -662,7 +746,7 @@ __device__ __forceinline__ void epi3b_body(const Launch& L, const MatDesc& d, in
                            b + 2 * CA + 3 * CB, ax, ar);
     __syncthreads();
   }
-  update_epilogue<WE, GT, FULL>(L, d, tm * WE::BM, tn * WE::BN, ax, ar);
+  update_epilogue<WE, GT, FULL, kEpiBatch>(L, d, tm * WE::BM, tn * WE::BN, ax, ar);
 }
 
 template <typename GT, bool VEC>
