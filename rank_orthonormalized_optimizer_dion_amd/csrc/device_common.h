@@ -253,14 +253,7 @@ __device__ __forceinline__ void bf_store_quad(u32x2* hi, u32x2* lo, int kq, int 
 }
 
 // Cell (x, k8) (16 bytes: elements k = 8 k8 .. 8 k8 + 7 of row x) of a
-// split-bfloat16 plane with `rows` rows, K-blocked by kPlaneK: the cells of
-// one kPlaneK slice of all rows are contiguous, row after row.
-__device__ __forceinline__ int64_t plane_cell(int64_t rows, int x, int k8) {
-  constexpr int CB = kPlaneK / 8;
-  return ((k8 / CB) * rows + x) * CB + k8 % CB;
-}
-
-// Cell (x, k8) of a split-bfloat16 plane with `rows` rows in row-major cell
+// split-bfloat16 plane with `rows` rows in row-major cell
 // order: the cells of one reduction column k8 of all rows are contiguous,
 // so 64 consecutive rows of one k8 are one 1 KB run (one direct-to-LDS
 // wavefront load).
@@ -337,10 +330,10 @@ __device__ __forceinline__ void bf_store_quad3(u32x2* hi, u32x2* mid, u32x2* lo,
 }
 
 // Loader of split-bfloat16 planes written ahead of time (hi and lo, zero
-// past the reduction length) in the K-blocked cell order of plane_cell():
-// the BK = kPlaneK slice of BX consecutive rows is one contiguous run of
-// 16-byte cells, read with one 16-byte load per cell and plane and stored
-// to LDS in the BfShape layout.  FULL: every row x of the tile exists.
+// past the reduction length) in plane_cell_r order, through registers: one
+// 16-byte load per cell and plane (consecutive rows of one k8 are
+// contiguous), stored to LDS in the BfShape layout.  FULL: every row x of
+// the tile exists.
 template <int BX, int BK, int NT = kThreads>
 struct LoadPl {
   static_assert(BK == kPlaneK, "one plane block per reduction tile");
@@ -362,7 +355,7 @@ struct LoadPl {
     for (int s = 0; s < NV; ++s) {
       const int idx = threadIdx.x + NT * s;
       const int k8 = idx % K8, x = idx / K8;
-      const int64_t o = plane_cell(rows, x0 + x, k0 / 8 + k8);
+      const int64_t o = plane_cell_r(rows, x0 + x, k0 / 8 + k8);
       if (FULL || x0 + x < xmax) {
         vh[s] = hi[o];
         vl[s] = lo[o];
@@ -949,6 +942,34 @@ __device__ __forceinline__ void pipeline_bf(LA& a, LB& b, int kbase, int nk, u32
     u32x4* base = smem + (kt & 1) * STAGE;
     mma(base, base + CA, base + 2 * CA, base + 2 * CA + CB);
     if (more) store((kt + 1) & 1);
+    __syncthreads();
+  }
+}
+
+// pipeline_bf with the B operand (planes written ahead of time) copied
+// straight into LDS by LoadDma: the next tile's B copies are issued with
+// its A loads, run during this tile's MFMAs and are waited for at the
+// barrier that ends the step; only A goes through registers.
+template <int BM, int BN, int BK, bool FULL, class LA, class LB, class MMA>
+__device__ __forceinline__ void pipeline_bf_dma(LA& a, const LB& b, int kbase, int nk, u32x4* smem,
+                                                MMA&& mma) {
+  constexpr int CA = BfShape<BM, BK>::CELLS, CB = BfShape<BN, BK>::CELLS;
+  constexpr int STAGE = 2 * (CA + CB);
+  if (nk <= 0) return;
+  b.issue(kbase, smem + 2 * CA, smem + 2 * CA + CB);
+  a.template load<FULL>(kbase);
+  a.store_bf(reinterpret_cast<u32x2*>(smem), reinterpret_cast<u32x2*>(smem + CA));
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    u32x4* next = smem + ((kt + 1) & 1) * STAGE;
+    if (more) {
+      b.issue(kbase + (kt + 1) * BK, next + 2 * CA, next + 2 * CA + CB);
+      a.template load<FULL>(kbase + (kt + 1) * BK);
+    }
+    const u32x4* cur = smem + (kt & 1) * STAGE;
+    mma(cur, cur + CA, cur + 2 * CA, cur + 2 * CA + CB);
+    if (more) a.store_bf(reinterpret_cast<u32x2*>(next), reinterpret_cast<u32x2*>(next + CA));
     __syncthreads();
   }
 }

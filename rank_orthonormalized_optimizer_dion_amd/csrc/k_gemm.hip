@@ -573,12 +573,12 @@ __device__ __forceinline__ void mv3b_body(const Launch& L, const MatDesc& d, con
   constexpr int BK = 32;
   const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
   LoadKC<WB::BM, BK, VEC, false, SrcM<GT>, WB::NT> la(sm, d.n, tm * WB::BM, d.m, kend);
-  const uint16_t* vt = reinterpret_cast<const uint16_t*>(L.ws + d.oH);
-  LoadPl<WB::BN, BK, WB::NT> lb(vt, vt + static_cast<int64_t>(d.r) * plane_pitch(d.n), d.r,
-                                tn * WB::BN, d.r);
+  const u32x4* vt = reinterpret_cast<const u32x4*>(L.ws + d.oH);
+  const LoadDma<WB::BN, BK, WB::NT> lb{vt, vt + static_cast<int64_t>(d.r) * plane_pitch(d.n) / 8, d.r,
+                                       tn * WB::BN, d.r};
   f32x16 acc[WB::FM][WB::FN];
   zero_acc(acc);
-  pipeline_bf<WB::BM, WB::BN, BK, FULL>(
+  pipeline_bf_dma<WB::BM, WB::BN, BK, FULL>(
       la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem,
       [&](const u32x4* ah, const u32x4* al, const u32x4* bh, const u32x4* bl) {
         mma_tile_bf3w<WB, BK>(ah, al, bh, bl, acc);
@@ -617,12 +617,12 @@ __device__ __forceinline__ void mtu3b_body(const Launch& L, const MatDesc& d, co
   constexpr int BK = 32;
   const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
   LoadXC<WB::BM, BK, VEC, SrcM<GT>, WB::NT> la(sm, d.n, tm * WB::BM, d.n, kend);
-  const uint16_t* ut = reinterpret_cast<const uint16_t*>(L.ws + d.oH);
-  LoadPl<WB::BN, BK, WB::NT> lb(ut, ut + static_cast<int64_t>(d.r) * plane_pitch(d.m), d.r,
-                                tn * WB::BN, d.r);
+  const u32x4* ut = reinterpret_cast<const u32x4*>(L.ws + d.oH);
+  const LoadDma<WB::BN, BK, WB::NT> lb{ut, ut + static_cast<int64_t>(d.r) * plane_pitch(d.m) / 8, d.r,
+                                       tn * WB::BN, d.r};
   f32x16 acc[WB::FM][WB::FN];
   zero_acc(acc);
-  pipeline_bf<WB::BM, WB::BN, BK, FULL>(
+  pipeline_bf_dma<WB::BM, WB::BN, BK, FULL>(
       la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem,
       [&](const u32x4* ah, const u32x4* al, const u32x4* bh, const u32x4* bl) {
         mma_tile_bf3w<WB, BK>(ah, al, bh, bl, acc);

@@ -94,10 +94,11 @@ __global__ __launch_bounds__(kThreads) void k_colscale(Launch L) {
 }
 
 // Q^T (r x rows, from Q: rows x r float32; Q = V for which = 0, U for
-// which = 1) as hi / lo bfloat16 planes of row pitch plane_pitch(rows)
-// (zero past column rows) in the K-blocked cell order of plane_cell(),
-// split as BfShape describes, so that M V and M^T U read their rank-r
-// operand as contiguous runs of 16-byte cells of 8 consecutive rows of Q.  One workgroup per 64 x 64 tile of Q: coalesced float4 row
+// which = 1) as hi / lo bfloat16 planes of plane_pitch(rows) columns (zero
+// past column rows) in plane_cell_r order, split as BfShape describes: a
+// cell holds 8 consecutive rows of one column of Q, and the cells of one
+// group of 8 rows are contiguous over the r columns, so that M V and
+// M^T U copy their rank-r operand straight into LDS.  One workgroup per 64 x 64 tile of Q: coalesced float4 row
 // reads into LDS, then each thread splits two cells (8 rows of one column).
 __global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
   constexpr int T = kSplitTile;
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
 #pragma unroll
   for (int s = 0; s < T * T / 8 / kThreads; ++s) {
     const int c = threadIdx.x + kThreads * s;
-    const int j = c / (T / 8), i = 8 * (c % (T / 8));
+    const int j = c % T, i = 8 * (c / T);   // consecutive threads: consecutive columns j
     if (j0 + j >= d.r || i0 + i >= kp) continue;
     f32x4 a, b;
 #pragma unroll
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_split_t(Launch L) {
     u32x2 ha, la, hb, lb;
     bf_split4(a, ha, la);
     bf_split4(b, hb, lb);
-    const int64_t o = plane_cell(d.r, j0 + j, (i0 + i) / 8);
+    const int64_t o = plane_cell_r(d.r, j0 + j, (i0 + i) / 8);
     gptr<u32x4> ph = (gptr<u32x4>)to_global(hi);
     ph[o] = u32x4{ha.x, ha.y, hb.x, hb.y};
     ph[plane / 8 + o] = u32x4{la.x, la.y, lb.x, lb.y};
