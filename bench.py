@@ -3,7 +3,7 @@ Llama-shaped stack (28 layers, 196 matrices: Q/O 3072x3072, K/V 3072x1024,
 gate/up 3072x8192, down 8192x3072; float32 X, R, V; bfloat16 G) on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant orth]
-                    [--rank-div 4] [--extra] [--no-cpu]
+                    [--rank-div 4] [--extra] [--configs] [--no-cpu]
 
 One step = one grouped libdion step over all 196 matrices (every phase of
 the method).  Inputs are synthetic, drawn on the device before timing.
@@ -242,6 +242,53 @@ def cpu_baseline(wl, variant: str, layers: int):
                       f"one {variant} step each in numpy float64, {total:.1f} s, scaled x{scale:g}"}
 
 
+def step_roofline(shapes, variant: str, eg: int, math: str):
+    """Whole-step roofline time: the three products at the chosen
+    arithmetic's matrix peak (ops per flop included), orth at the float32
+    matrix peak, against the compulsory bytes at the HBM peak.  Returns
+    (T_roof, T_mfma, flops, compulsory bytes)."""
+    f, _ = phase_model(shapes, variant, eg)
+    flops, bmin = step_model(shapes, variant, eg)
+    peak, ops = MATH[math]
+    f_prod = f["mv"] + f["mtu"] + f["update"]
+    t_mfma = ops * f_prod / peak + (flops - f_prod) / MFMA_F32_PEAK
+    return max(bmin / HBM_PEAK, t_mfma), t_mfma, flops, bmin
+
+
+# the other workloads: (label, config number, rank for config 5, timed steps)
+OTHER_CONFIGS = (("single-256x128", 1, None, 200), ("planted-2048", 2, None, 40),
+                 ("gpt160m-stack", 3, None, 30), ("mlp70b-r512", 5, 512, 10),
+                 ("mlp70b-r2048", 5, 2048, 10))
+
+
+def time_configs(dion, torch, dev, math: str):
+    """steps/s of both variants on every other workload, with the fraction
+    of the whole-step roofline each reaches."""
+    from workloads import config
+    from workloads.device import DeviceMatrix
+    out = {}
+    for label, num, r, steps in OTHER_CONFIGS:
+        wl = config(num, r=r) if r else config(num)
+        print(f"[bench] {wl.name}", file=sys.stderr, flush=True)
+        mats = [DeviceMatrix(wl, s, dev) for s in wl.mats]
+        torch.cuda.synchronize()
+        shapes = [(s.m, s.n, s.r) for s in wl.mats]
+        eg = 2 if wl.g_dtype == "bf16" else 4
+        for var in ("orth", "dion"):
+            sec, _ = time_plan(dion, torch, mats, var, steps, 3, wl.eta, wl.beta, math)
+            t_roof, t_mfma, flops, bmin = step_roofline(shapes, var, eg, math)
+            out[f"{label}_{var}"] = {
+                "workload": wl.name, "steps_per_s": round(1 / sec, 2),
+                "ms_per_step": round(sec * 1e3, 4),
+                "bound": "mfma" if t_mfma >= bmin / HBM_PEAK else "hbm",
+                "roofline_frac": round(t_roof / sec, 4),
+                "effective_tflops": round(flops / sec / 1e12, 2),
+                "effective_gbps": round(bmin / sec / 1e9, 1)}
+        del mats
+        torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +303,9 @@ def main(argv=None) -> int:
     ap.add_argument("--extra", action="store_true",
                     help="also time the other variant and rank fraction")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time both variants on the other workloads (single matrices, "
+                         "the 160M stack, the 70B MLP matrix) under \"configs\"")
     ap.add_argument("--cpu-layers", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (a known byte "
@@ -304,13 +354,7 @@ def main(argv=None) -> int:
     traffic = measured_traffic(kernel, wl.name) if kernel.startswith("k_") else None
     roof = roofline_of(dom, phases[dom], f, b, traffic, args.math)
     roof["kernel"] = kernel
-    flops, bmin = step_model(shapes, args.variant, eg)
-    # whole-step roofline: the three products at the chosen arithmetic's
-    # peak (ops per flop included), orth at the float32 matrix peak
-    peak, ops = MATH[args.math]
-    f_prod = f["mv"] + f["mtu"] + f["update"]
-    t_mfma = ops * f_prod / peak + (flops - f_prod) / MFMA_F32_PEAK
-    t_roof = max(bmin / HBM_PEAK, t_mfma)
+    t_roof, t_mfma, flops, bmin = step_roofline(shapes, args.variant, eg, args.math)
     out = {
         "metric": "Dion/Orth-Dion steps/sec + effective HBM GB/s (% roofline), 3B-shaped stack",
         "value": round(1.0 / sec, 4),
@@ -375,6 +419,8 @@ def main(argv=None) -> int:
         out["extra"] = extra
     del mats
     torch.cuda.empty_cache()
+    if args.configs:
+        out["configs"] = time_configs(dion, torch, dev, args.math)
     if not args.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.variant, args.cpu_layers)

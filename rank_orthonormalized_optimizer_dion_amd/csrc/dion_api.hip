@@ -34,6 +34,8 @@ constexpr size_t kAlign = 256;
 constexpr int kTargetBlocks = 1024;   // split the reduction below this many tiles
 constexpr int kMinSplitLen = 256;     // shortest reduction slice worth a split
 constexpr int kBK = 32;
+constexpr int kBlockThreads = 256;  // threads of every libdion workgroup
+constexpr int kColnormRows = 512;   // fewest rows per column-norm slice
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
@@ -56,6 +58,8 @@ struct ClassRec {
   int bn_mv;   // M V tile: bn_r, or 256 (256 x 256 split-bfloat16 tiles)
   int bn_mtu;  // M^T U tile, likewise
   int s_mv, kl_mv, s_mtu, kl_mtu, s_gp, kl_gp, s_gw, kl_gw;
+  int s_cn, kl_cn;  // Dion column norms: row slices (<= 64, so the slices'
+                    // float64 sums fit the Gram area, rp^2 >= 64 r) and rows per slice
 };
 
 }  // namespace
@@ -202,6 +206,9 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
       k.kl_gp = cdiv(k.m, kBK) * kBK;
     }
     pick_split(t_gw, k.n, k.s_gw, k.kl_gw);
+    k.s_cn = std::min(64, std::max(1, cdiv(k.n, kColnormRows)));
+    k.kl_cn = cdiv(k.n, k.s_cn);
+    k.s_cn = cdiv(k.n, k.kl_cn);
   }
   // Workspace: status words | matrix table (grouped calls) | per-matrix buffers.
   size_t off = 0;
@@ -448,9 +455,16 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   } else {
     base.flag = DION_STATUS_COLNORM;
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-      ci.tiles = cdiv(c.r, 64);
+      ci.tiles = cdiv(c.r, 64) * c.s_cn;
+      ci.splits = c.s_cn;
+      ci.klen = c.kl_cn;
       return true;
     }, [&](const Launch& L) { return launch_colnorm(L, st); }));
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      ci.tiles = cdiv(c.r, kBlockThreads);
+      ci.splits = c.s_cn;
+      return true;
+    }, [&](const Launch& L) { return launch_colnorm_fin(L, st); }));
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       ci.tiles = cdiv(static_cast<int64_t>(c.n) * c.r, ept);
       return true;

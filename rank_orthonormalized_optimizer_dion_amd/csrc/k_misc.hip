@@ -1,6 +1,7 @@
 // Small bandwidth kernels of the step:
 //   k_reduce    sum of split-K partial products, in a fixed order
-//   k_colnorm   Dion's rule, part 1: inverse Euclidean norms of W's columns
+//   k_colnorm   Dion's rule, part 1: sums of squares of W's columns, per row slice
+//   k_colnorm_fin  inverse Euclidean norms from the slices
 //   k_colscale  Dion's rule, part 2: Vbar = W diag(1/||w_j||) written into V
 //   k_split_t   split-bfloat16 planes of V^T for M V, of U^T for M^T U
 //   k_split_n   split-bfloat16 planes of U, W and Vbar for the fused update
@@ -43,8 +44,12 @@ __global__ __launch_bounds__(kThreads) void k_reduce(Launch L) {
   }
 }
 
-// One workgroup per 64 columns: 4 row groups accumulate squares in float64,
-// then combine in a fixed order.
+// Column sums of squares of W in float64, split over rows so that one
+// matrix of few columns still fills the GPU: work item (slice sp, column
+// group cg) covers rows [sp klen, (sp + 1) klen) of 64 columns, 4 row
+// groups accumulate and combine in a fixed order, and the slice's sums go
+// to row sp of a (splits x r) float64 array in the Gram area (free by
+// now: the factorization of P has consumed it).
 __global__ __launch_bounds__(kThreads) void k_colnorm(Launch L) {
   __shared__ double red[4][64];
   MatDesc d;
@@ -52,26 +57,43 @@ __global__ __launch_bounds__(kThreads) void k_colnorm(Launch L) {
   int local;
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
+  const int groups = (d.r + 63) / 64;
+  const int sp = local / groups, cg = local - sp * groups;
   const float* W = reinterpret_cast<const float*>(L.ws + d.oW);
-  float* inv = reinterpret_cast<float*>(L.ws + d.oN);
-  const int col = local * 64 + (threadIdx.x & 63);
+  double* part = reinterpret_cast<double*>(L.ws + d.oS);
+  const int col = cg * 64 + (threadIdx.x & 63);
   const int rg = threadIdx.x >> 6;
+  const int i0 = sp * ci.klen, i1 = min(d.n, i0 + ci.klen);
   double acc = 0.0;
   if (col < d.r)
-    for (int i = rg; i < d.n; i += 4) {
+    for (int i = i0 + rg; i < i1; i += 4) {
       const double w = W[static_cast<int64_t>(i) * d.r + col];
       acc += w * w;
     }
   red[rg][threadIdx.x & 63] = acc;
   __syncthreads();
-  if (rg == 0 && col < d.r) {
-    const double s = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) +
-                     red[3][threadIdx.x];
-    if (!(s > 0.0) || !(s < INFINITY)) {
-      atomicOr(&L.status[d.slot], L.flag);
-    } else {
-      inv[col] = static_cast<float>(1.0 / sqrt(s));
-    }
+  if (rg == 0 && col < d.r)
+    part[static_cast<int64_t>(sp) * d.r + col] =
+        ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
+}
+
+// Inverse column norms from the slices' sums, added in slice order; a zero
+// or non-finite norm is a breakdown.
+__global__ __launch_bounds__(kThreads) void k_colnorm_fin(Launch L) {
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int col = local * kThreads + threadIdx.x;
+  if (col >= d.r) return;
+  const double* part = reinterpret_cast<const double*>(L.ws + d.oS);
+  double s = 0.0;
+  for (int sp = 0; sp < ci.splits; ++sp) s += part[static_cast<int64_t>(sp) * d.r + col];
+  if (!(s > 0.0) || !(s < INFINITY)) {
+    atomicOr(&L.status[d.slot], L.flag);
+  } else {
+    reinterpret_cast<float*>(L.ws + d.oN)[col] = static_cast<float>(1.0 / sqrt(s));
   }
 }
 
@@ -249,6 +271,7 @@ hipError_t go(K kernel, const Launch& L, hipStream_t st) {
 int elems_per_tile() { return kElemsPerTile; }
 hipError_t launch_reduce(const Launch& L, hipStream_t st) { return go(k_reduce, L, st); }
 hipError_t launch_colnorm(const Launch& L, hipStream_t st) { return go(k_colnorm, L, st); }
+hipError_t launch_colnorm_fin(const Launch& L, hipStream_t st) { return go(k_colnorm_fin, L, st); }
 hipError_t launch_colscale(const Launch& L, hipStream_t st) { return go(k_colscale, L, st); }
 hipError_t launch_split_t(const Launch& L, hipStream_t st) { return go(k_split_t, L, st); }
 hipError_t launch_split_n(const Launch& L, hipStream_t st) { return go(k_split_n, L, st); }

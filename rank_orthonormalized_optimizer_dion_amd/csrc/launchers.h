@@ -25,6 +25,7 @@ hipError_t launch_chol_trail(const Launch& L, hipStream_t st);
 
 hipError_t launch_reduce(const Launch& L, hipStream_t st);
 hipError_t launch_colnorm(const Launch& L, hipStream_t st);
+hipError_t launch_colnorm_fin(const Launch& L, hipStream_t st);
 hipError_t launch_colscale(const Launch& L, hipStream_t st);
 // V^T (which = 0) or U^T (which = 1) split-bfloat16 planes, in
 // kSplitTile x kSplitTile tiles of V or U
