@@ -167,3 +167,18 @@ def test_plan_api_matches_step_batched(gpu_lib):
     for ta, tb in zip(a, b):
         for u, w in zip(ta, tb):
             assert torch.equal(u, w)
+
+
+# Wide W (n >> m): Dion's column norms run in up to 64 row slices of W with a
+# ragged last slice, over whole and partial 64-column groups.
+@pytest.mark.parametrize("m,n,r", [(48, 33001, 24), (160, 9000, 130)])
+@pytest.mark.parametrize("variant", [ORTH, DION])
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+def test_wide_right_factor(gpu_lib, m, n, r, variant, arith):
+    wl = _wl(m, n, r, "bf16")
+    c = Case(wl, wl.mats[0])
+    c.load_grad(0)
+    say(f"wide {m}x{n} r={r} {variant} {arith}")
+    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant, math=arith)
+    res, x_prev = c.oracle(variant)
+    assert_close(c.errors(x_prev, res.M), TOL_1, f"wide {m}x{n} r={r} {variant} {arith}")
