@@ -118,6 +118,27 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
 // rewritten two steps later, after every thread has passed the barrier that
 // follows its last read).  A failed pivot is flagged in the same buffer, so
 // every wavefront leaves the loop at the same step.
+// Lane `k` (wavefront-uniform) of a float64 register, without the LDS
+// round trip of a shuffle.
+__device__ __forceinline__ double read_lane(double v, int k) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(u), k);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), k);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// 1 / sqrt(x) for a positive normal x: the hardware estimate refined by two
+// Newton-Raphson steps y <- y (3 - x y^2) / 2, each of which doubles the
+// number of correct bits (to full float64 precision from an estimate good
+// to 2^-14 or better).  Replaces a square root and a division on the
+// factorization's serial path.
+__device__ __forceinline__ double rsqrt_nr(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * fma(-0.5 * x, y * y, 1.5);
+  y = y * fma(-0.5 * x, y * y, 1.5);
+  return y;
+}
+
 __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
   __shared__ double rowA[2][NB];
   __shared__ double rowZ[2][NB];
@@ -143,12 +164,13 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
   bool bad = false;
 #pragma unroll
   for (int q = 0; q < NB / 4; ++q) {
+#pragma nounroll
     for (int w = 0; w < 4; ++w) {
       const int k = 4 * q + w, buf = k & 1;
       if (wave == w) {   // this wavefront holds row k
-        const double dk = __shfl(a[q], k, 64);
+        const double dk = read_lane(a[q], k);
         const bool ok = dk > kPivotTol * sd[k] && dk < INFINITY;
-        const double t = sqrt(dk), inv = 1.0 / t;
+        const double inv = rsqrt_nr(dk), t = dk * inv;
         a[q] = lane > k ? a[q] * inv : (lane == k ? t : 0.0);
         z[q] = lane <= k ? z[q] * inv : 0.0;
         rowA[buf][lane] = a[q];
@@ -156,17 +178,21 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
         if (lane == 0) badf[buf] = ok ? 0 : 1;
       }
       __syncthreads();
-      if (badf[buf]) {
+      // every read of the broadcast row is issued before the first use
+      const int flag = badf[buf];
+      const double rj = rowA[buf][lane], zj = rowZ[buf][lane];
+      double ai[NB / 4];
+#pragma unroll
+      for (int qq = q; qq < NB / 4; ++qq) ai[qq] = rowA[buf][4 * qq + wave];
+      if (flag) {
         bad = true;
         break;
       }
-      const double rj = rowA[buf][lane], zj = rowZ[buf][lane];
 #pragma unroll
       for (int qq = q; qq < NB / 4; ++qq) {
         if (qq == q && wave <= w) continue;   // rows 4 qq + wave <= k
-        const double ai = rowA[buf][4 * qq + wave];
-        if (lane > k) a[qq] -= ai * rj;
-        z[qq] -= ai * zj;
+        if (lane > k) a[qq] -= ai[qq] * rj;
+        z[qq] -= ai[qq] * zj;
       }
     }
     if (bad) break;
