@@ -327,20 +327,37 @@ hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
     ci.tiles = nb * (nb + 1) / 2;
     return true;
   }, [&](const Launch& L) { return launch_chol_init(L, st); }));
-  for (int kb = 0; kb < max_nblk; ++kb) {
+  // block steps in pairs (kb, kb + 1) with look-ahead: factor kb, bring
+  // block row kb + 1 up to date, factor kb + 1, then one trailing pass with
+  // both panels
+  auto diag_panel = [&](int kb) -> hipError_t {
     base.kb = kb;
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       ci.tiles = c.rp / kCholNB > kb ? 1 : 0;
       return true;
     }, [&](const Launch& L) { return launch_chol_diag(L, st); }));
-    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+    return grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       const int nb = c.rp / kCholNB;
       ci.tiles = nb > kb ? nb - 1 : 0;
       return true;
-    }, [&](const Launch& L) { return launch_chol_panel(L, st); }));
+    }, [&](const Launch& L) { return launch_chol_panel(L, st); });
+  };
+  for (int kb = 0; kb < max_nblk; kb += 2) {
+    DION_TRY(diag_panel(kb));
+    if (kb + 1 >= max_nblk) break;
+    base.kb = kb;
+    base.mode = 1;
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       const int nl = c.rp / kCholNB - kb - 1;
-      ci.tiles = nl > 0 ? nl * (nl + 1) / 2 + nl * (kb + 1) : 0;
+      ci.tiles = nl > 0 ? nl + kb + 1 : 0;
+      return true;
+    }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
+    DION_TRY(diag_panel(kb + 1));
+    base.kb = kb;
+    base.mode = 2;
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      const int nl = c.rp / kCholNB - kb - 2;
+      ci.tiles = nl > 0 ? nl * (nl + 1) / 2 + nl * (kb + 2) : 0;
       return true;
     }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
   }

@@ -66,6 +66,7 @@ struct Launch {
   int32_t which;          // 0: factor P (m rows), 1: factor W (n rows)
   int32_t pass;           // CholeskyQR pass 1 or 2
   int32_t flag;           // status bit of this factorization
+  int32_t mode;           // Cholesky trailing update: 1 look-ahead block row, 2 the rest
 };
 
 }  // namespace dion

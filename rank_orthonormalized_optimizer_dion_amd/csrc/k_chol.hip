@@ -8,7 +8,12 @@
 // Per block step kb (host loop):
 //   k_chol_diag   factor the diagonal block, Dinv = T_kk^{-1}, Y_kk = T_kk^{-T}
 //   k_chol_panel  T_kj = T_kk^{-T} A_kj (j > kb);  Y_kc = T_kk^{-T} Y_kc (c < kb)
-//   k_chol_trail  A_ij -= T_ki^T T_kj (kb < i <= j);  Y_ic -= T_ki^T Y_kc (c <= kb)
+//   k_chol_trail  A_ij -= T_ki^T T_kj (kb < i <= j);  Y_ic -= T_ki^T Y_kc (c <= kb),
+//                 with look-ahead: block steps run in pairs (kb, kb + 1); mode 1
+//                 updates block row kb + 1 alone with panel kb, so that block
+//                 kb + 1 can be factored, and mode 2 then updates block rows
+//                 kb + 2 on with both panels at once (128 reduction rows), one
+//                 pass over the trailing matrix per two block steps
 // k_chol_init sums the Gram partials into A (float64) first and pads the
 // rows past r with the identity.
 #include <math.h>
@@ -36,14 +41,14 @@ __device__ __forceinline__ double* dptr(const Launch& L, int64_t off) {
   return reinterpret_cast<double*>(L.ws + off);
 }
 
-// C = L^T R for 64 x 64 blocks over 64 reduction rows, C[i][j] =
+// C += L^T R for 64 x 64 blocks over 64 reduction rows, C[i][j] +=
 // sum_e L[e][i] R[e][j] (L, R row-major with pitches ll, lr), on the
 // 16 x 16 x 4 float64 MFMA: 2 x 2 wavefronts of 32 x 32, each lane loading
 // its own operands from memory (lane l: row 4 s + l / 16, column l % 16 of
 // a 16-wide column strip, 16 consecutive doubles per 16 lanes).  All loads
 // of a wavefront are issued before its first MFMA.
-__device__ __forceinline__ void block_tn(const double* Lp, int64_t ll, const double* Rp, int64_t lr,
-                                         f64x4 (&acc)[2][2]) {
+__device__ __forceinline__ void block_tn_add(const double* Lp, int64_t ll, const double* Rp,
+                                             int64_t lr, f64x4 (&acc)[2][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4;
   const int ci = (wave >> 1) * 32 + (lane & 15), cj = (wave & 1) * 32 + (lane & 15);
@@ -58,16 +63,22 @@ __device__ __forceinline__ void block_tn(const double* Lp, int64_t ll, const dou
       b[s][f] = R[(4 * s + g) * lr + cj + 16 * f];
     }
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
   for (int s = 0; s < NB / 4; ++s)
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn)
         acc[fm][fn] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s][fm], b[s][fn], acc[fm][fn], 0, 0, 0);
+}
+
+// C = L^T R (block_tn_add from zero).
+__device__ __forceinline__ void block_tn(const double* Lp, int64_t ll, const double* Rp, int64_t lr,
+                                         f64x4 (&acc)[2][2]) {
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = f64x4{0.0, 0.0, 0.0, 0.0};
+  block_tn_add(Lp, ll, Rp, lr, acc);
 }
 
 // Offset of the element lane holds in register v of output block (fm, fn)
@@ -236,7 +247,15 @@ __global__ __launch_bounds__(kThreads) void k_chol_panel(Launch L) {
       for (int v = 0; v < 4; ++v) out[block_off(fm, fn, v, rp)] = acc[fm][fn][v];
 }
 
-// Trailing update of the factorization and of the identity block columns.
+// Trailing update of the factorization and of the identity block columns,
+// for the block-step pair (kb, kb + 1).  Rows kb and kb + 1 of T (and of Y)
+// are 128 consecutive rows, so the two panels form one 128-row reduction.
+//   mode 1: block row kb + 1 with panel kb: A_(kb+1)j for j > kb and
+//           Y_(kb+1)c for c <= kb (first write at c = kb).
+//   mode 2: block rows i >= kb + 2 with panels kb and kb + 1: A_ij for
+//           j >= i, and Y_ic for c <= kb + 1.  Y_kb,(kb+1) lies above Y's
+//           diagonal and is never written, so column block kb + 1 takes the
+//           second panel only; Y_i,kb and Y_i,(kb+1) are first writes.
 __global__ __launch_bounds__(kThreads) void k_chol_trail(Launch L) {
   MatDesc d;
   ClassInfo ci;
@@ -245,34 +264,56 @@ __global__ __launch_bounds__(kThreads) void k_chol_trail(Launch L) {
   if (skipped(L, d)) return;
   const int kb = L.kb, nblk = d.rp / NB;
   const int64_t rp = d.rp, o = static_cast<int64_t>(kb) * NB;
-  const int nl = nblk - kb - 1;
-  const int nsym = nl * (nl + 1) / 2;
   double* A = dptr(L, d.oA);
   double* Y = dptr(L, d.oY);
-  const double* left;
+  const double* left;   // T rows of the panel(s), column block bi
   const double* rgt;
   double* out;
-  bool assign = false;
-  if (local < nsym) {
-    int p = local, i = 0;
-    while (p >= nl - i) {
-      p -= nl - i;
-      ++i;
+  bool assign = false, both = false, second_only = false;
+  if (L.mode == 1) {
+    const int nl = nblk - kb - 1, bi = kb + 1;
+    left = A + o * rp + bi * NB;
+    if (local < nl) {
+      rgt = A + o * rp + (bi + local) * NB;
+      out = A + static_cast<int64_t>(bi) * NB * rp + (bi + local) * NB;
+    } else {
+      const int c = local - nl;
+      rgt = Y + o * rp + c * NB;
+      out = Y + static_cast<int64_t>(bi) * NB * rp + c * NB;
+      assign = c == kb;
     }
-    const int bi = kb + 1 + i, bj = bi + p;
-    left = A + o * rp + bi * NB;
-    rgt = A + o * rp + bj * NB;
-    out = A + static_cast<int64_t>(bi) * NB * rp + bj * NB;
   } else {
-    const int t = local - nsym;
-    const int bi = kb + 1 + t / (kb + 1), c = t % (kb + 1);
-    left = A + o * rp + bi * NB;
-    rgt = Y + o * rp + c * NB;
-    out = Y + static_cast<int64_t>(bi) * NB * rp + c * NB;
-    assign = c == kb;   // first write of this block of Y
+    const int nl = nblk - kb - 2;
+    const int nsym = nl * (nl + 1) / 2;
+    both = true;
+    if (local < nsym) {
+      int p = local, i = 0;
+      while (p >= nl - i) {
+        p -= nl - i;
+        ++i;
+      }
+      const int bi = kb + 2 + i, bj = bi + p;
+      left = A + o * rp + bi * NB;
+      rgt = A + o * rp + bj * NB;
+      out = A + static_cast<int64_t>(bi) * NB * rp + bj * NB;
+    } else {
+      const int t = local - nsym;
+      const int bi = kb + 2 + t / (kb + 2), c = t % (kb + 2);
+      left = A + o * rp + bi * NB;
+      rgt = Y + o * rp + c * NB;
+      out = Y + static_cast<int64_t>(bi) * NB * rp + c * NB;
+      assign = c >= kb;
+      second_only = c == kb + 1;
+    }
   }
   f64x4 acc[2][2];
-  block_tn(left, rp, rgt, rp, acc);
+  const int64_t next = static_cast<int64_t>(NB) * rp;   // the second panel's rows
+  if (second_only) {
+    block_tn(left + next, rp, rgt + next, rp, acc);
+  } else {
+    block_tn(left, rp, rgt, rp, acc);
+    if (both) block_tn_add(left + next, rp, rgt + next, rp, acc);
+  }
   gptr<double> q = to_global(out);
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm)
