@@ -50,6 +50,9 @@ SHAPES = [
     (1, 7, 1), (9, 1, 1), (131, 67, 3), (512, 384, 128), (130, 390, 65), (1000, 37, 20),
     # ranks that take the 256 x 256 split-bfloat16 M V tiles, ragged in m, n and r
     (700, 300, 250), (520, 1000, 480),
+    # odd numbers of 64-wide Cholesky blocks (3 and 5): the look-ahead pairs
+    # end with an unpaired block step
+    (400, 300, 150), (700, 650, 300),
 ]
 
 
@@ -182,3 +185,21 @@ def test_wide_right_factor(gpu_lib, m, n, r, variant, arith):
     gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant, math=arith)
     res, x_prev = c.oracle(variant)
     assert_close(c.errors(x_prev, res.M), TOL_1, f"wide {m}x{n} r={r} {variant} {arith}")
+
+
+# One grouped call over classes of 1, 3, 4 and 5 Cholesky blocks: the
+# look-ahead pairs run for all classes together, and each class's block
+# steps stop at its own last block.
+@pytest.mark.parametrize("variant", [ORTH, DION])
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+def test_batched_mixed_block_counts(gpu_lib, variant, arith):
+    shapes = [(400, 300, 150), (256, 192, 48), (700, 650, 300), (300, 260, 250)]
+    cases = [Case(_wl(m, n, r, "bf16", seed=80 + i), MatrixSpec(0, "W", 0, m, n, r))
+             for i, (m, n, r) in enumerate(shapes)]
+    for c in cases:
+        c.load_grad(0)
+    say(f"mixed block counts {variant} {arith}")
+    gpu_lib.step_batched([(c.X, c.G, c.R, c.V) for c in cases], 0.01, 0.95, variant, math=arith)
+    for c, (m, n, r) in zip(cases, shapes):
+        res, x_prev = c.oracle(variant)
+        assert_close(c.errors(x_prev, res.M), TOL_1, f"mixed {m}x{n} r={r} {variant} {arith}")
