@@ -111,8 +111,10 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
     const int gi = bi * NB + e / NB, gj = bj * NB + e % NB;
     double v;
     if (gi < d.r && gj < d.r) {
+      // the Gram kernel writes the upper triangle (gi <= gj) only
+      const int64_t e = static_cast<int64_t>(min(gi, gj)) * rp + max(gi, gj);
       v = 0.0;
-      for (int s = 0; s < ci.splits; ++s) v += S[s * plane + gi * rp + gj];
+      for (int s = 0; s < ci.splits; ++s) v += S[s * plane + e];
     } else {
       v = gi == gj ? 1.0 : 0.0;
     }

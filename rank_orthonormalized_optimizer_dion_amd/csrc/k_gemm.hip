@@ -263,12 +263,20 @@ __device__ __forceinline__ void gram_body(const Launch& L, const MatDesc& d, int
   for (int fm = 0; fm < FB; ++fm)
 #pragma unroll
     for (int fn = 0; fn < FB; ++fn) acc[fm][fn] = f64x4{0.0, 0.0, 0.0, 0.0};
-  pipeline<BG, BG, BK, FULL>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem,
-                             [&](const f32x4* a, const f32x4* b) { mma_tile_f64<BG, BK>(a, b, acc); });
-  gptr<double> out = to_global(reinterpret_cast<double*>(L.ws + d.oS) +
-                               static_cast<int64_t>(s) * d.rp * d.rp);
+  // On a diagonal tile the wavefront of rows BG/2.. and columns ..BG/2 lies
+  // wholly below the diagonal: it loads its share of the tile for the
+  // others but computes and stores nothing (the factorization reads the
+  // upper triangle only).
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const bool below = ti == tj && wm > wn;
+  pipeline<BG, BG, BK, FULL>(la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem,
+                             [&](const f32x4* a, const f32x4* b) {
+                               if (!below) mma_tile_f64<BG, BK>(a, b, acc);
+                             });
+  if (below) return;
+  gptr<double> out = to_global(reinterpret_cast<double*>(L.ws + d.oS) +
+                               static_cast<int64_t>(s) * d.rp * d.rp);
 #pragma unroll
   for (int fm = 0; fm < FB; ++fm)
 #pragma unroll
