@@ -219,12 +219,21 @@ def cpu_baseline(wl, variant: str, layers: int):
     import numpy as np
     from oracle import dion_step
     from workloads import MatrixStream
+    blas = "unknown BLAS"
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"), default=1)
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max((i.get("num_threads", 1) for i in libs), default=1)
+        if libs:
+            blas = f"{libs[0].get('internal_api', 'blas')} {libs[0].get('version', '')}".strip()
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     per_layer = sum(1 for s in wl.mats if s.layer == 0)
     sample = [s for s in wl.mats if s.layer < layers]
     total = 0.0
@@ -239,7 +248,8 @@ def cpu_baseline(wl, variant: str, layers: int):
     return {"value": round(1.0 / (total * scale), 6), "unit": "steps/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{len(sample)} of {len(wl.mats)} matrices (layer 0, {per_layer} roles), "
-                      f"one {variant} step each in numpy float64, {total:.1f} s, scaled x{scale:g}"}
+                      f"one {variant} step each in numpy float64 ({blas}, {cpu}), {total:.1f} s, "
+                      f"scaled x{scale:g}"}
 
 
 def step_roofline(shapes, variant: str, eg: int, math: str):
