@@ -37,7 +37,9 @@ struct MatDesc {
                      // cells (plane_cell_r), pitch plane_pitch(r); 0 if unused
   int64_t oH;        // split-bfloat16 planes (hi, then lo) of V^T during
                      // M V, of U^T during M^T U: r x plane_pitch(rows)
-                     // bfloat16 each, zero past the last row; 0 without them
+                     // bfloat16 each in plane_cell_r order (cell = 8
+                     // consecutive rows of V or U), zero past the last row;
+                     // 0 without them
 };
 
 // Matrices with the same (m, n, r) form a class; inside one launch every

@@ -710,10 +710,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_mtu3(Launch L) {
 // two per SIMD, each holding both products (U Vbar^T, U W^T).  The rank-r
 // factors come as split-bfloat16 planes written by k_split_n and are copied
 // straight into LDS.
-#ifndef DION_EPI_BATCH
-#define DION_EPI_BATCH 32
-#endif
-constexpr int kEpiBatch = DION_EPI_BATCH;
+constexpr int kEpiBatch = 32;   // epilogue elements per lane loaded before a batch's stores
 using WE = WGrid<256, 128, 4, 2>;
 
 template <typename GT, bool VEC, bool FULL>
