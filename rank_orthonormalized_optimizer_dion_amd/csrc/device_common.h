@@ -915,41 +915,12 @@ __device__ __forceinline__ void pipeline2_bf(LA& a0, LA& a1, LB& b0, LB& b1, int
 }
 
 // Two-stage split-bfloat16 pipeline for large tiles: LDS double-buffered,
-// one register set.  Tile kt+1's loads are issued before tile kt's MFMAs
-// and stored to the other LDS stage after them; one barrier per tile.
+// one barrier per tile.  The B operand (planes written ahead of time) is
+// copied straight into LDS by LoadDma; A goes through registers (loaded
+// before this tile's MFMAs, split and stored to the other stage after
+// them).  The next tile's B copies run during this tile's MFMAs and are
+// waited for at the barrier that ends the step.
 // smem: 2 stages of bf_stage_cells() 16-byte cells.
-template <int BM, int BN, int BK, bool FULL, class LA, class LB, class MMA>
-__device__ __forceinline__ void pipeline_bf(LA& a, LB& b, int kbase, int nk, u32x4* smem,
-                                            MMA&& mma) {
-  constexpr int CA = BfShape<BM, BK>::CELLS, CB = BfShape<BN, BK>::CELLS;
-  constexpr int STAGE = 2 * (CA + CB);
-  auto store = [&](int st) {
-    u32x4* base = smem + st * STAGE;
-    a.store_bf(reinterpret_cast<u32x2*>(base), reinterpret_cast<u32x2*>(base + CA));
-    b.store_bf(reinterpret_cast<u32x2*>(base + 2 * CA), reinterpret_cast<u32x2*>(base + 2 * CA + CB));
-  };
-  if (nk <= 0) return;
-  a.template load<FULL>(kbase);
-  b.template load<FULL>(kbase);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      a.template load<FULL>(kbase + (kt + 1) * BK);
-      b.template load<FULL>(kbase + (kt + 1) * BK);
-    }
-    u32x4* base = smem + (kt & 1) * STAGE;
-    mma(base, base + CA, base + 2 * CA, base + 2 * CA + CB);
-    if (more) store((kt + 1) & 1);
-    __syncthreads();
-  }
-}
-
-// pipeline_bf with the B operand (planes written ahead of time) copied
-// straight into LDS by LoadDma: the next tile's B copies are issued with
-// its A loads, run during this tile's MFMAs and are waited for at the
-// barrier that ends the step; only A goes through registers.
 template <int BM, int BN, int BK, bool FULL, class LA, class LB, class MMA>
 __device__ __forceinline__ void pipeline_bf_dma(LA& a, const LB& b, int kbase, int nk, u32x4* smem,
                                                 MMA&& mma) {
