@@ -292,8 +292,10 @@ __device__ __forceinline__ void gram_body(const Launch& L, const MatDesc& d, int
     }
 }
 
+// Four blocks per CU (at most 128 registers per lane): the float64 MFMAs
+// are long, and the extra wavefronts cover the tile loads and barriers.
 template <int BG, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_gram(Launch L) {
+__global__ __launch_bounds__(kThreads, 4) void k_gram(Launch L) {
   constexpr int BK = 32;
   __shared__ f32x4 smem[mainloop_cells<BG, BG, BK>()];
   MatDesc d;
