@@ -400,8 +400,9 @@ __device__ __forceinline__ void trmm6_body(const Launch& L, const MatDesc& d, in
   store_tile<BM, BN>(dst, d.r, tm * BM, tn * BN, rows, d.r, acc);
 }
 
+// Three blocks per CU (at most 168 registers per lane).
 template <int BN, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_trmm6(Launch L) {
+__global__ __launch_bounds__(kThreads, 3) void k_trmm6(Launch L) {
   constexpr int BK = 16;
   __shared__ u32x4 smem[2 * 3 * (BfShape<BM, BK>::CELLS + BfShape<BN, BK>::CELLS)];
   MatDesc d;
