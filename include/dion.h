@@ -76,11 +76,24 @@ extern "C" {
  *   hi = bf16(x) and lo = bf16(x - hi), and a product is taken as
  *   hi*hi + hi*lo + lo*hi on the bfloat16 matrix cores with float32
  *   accumulation: relative product error up to 2^-16 instead of 2^-24, at
- *   about five times the float32 matrix rate.  orth() (the Gram matrix in
- *   float64, the triangular product in float32) is unaffected. */
+ *   about five times the float32 matrix rate.  orth() (the Gram matrix
+ *   below, the triangular product in float32) is unaffected. */
 #define DION_MATH_F32     0x000
 #define DION_MATH_BF16X3  0x100
 #define DION_MATH_MASK    0x100
+
+/* Gram matrix S = Q^T Q of orth()'s CholeskyQR pass (orth() of equations 2
+ * and 4 of the Orth-Dion page), OR-ed into `variant` like the math mode.
+ * Default: each float32 column of Q is scaled by a power of two into
+ *   (-1, 1) and written as five signed base-128 digits (int8); S is
+ *   assembled in float64 from the 15 leading digit products, each summed
+ *   exactly in int32 on the int8 matrix cores.  Entry error about
+ *   2^-34 max|q_i| sum|q_j|, i.e. near 1e-11 relative for columns of a few
+ *   thousand entries; a non-finite entry of Q makes its row and column of S
+ *   NaN (a breakdown of the factorization).
+ * DION_GRAM_F64: float32 products summed in float64 on the float64 matrix
+ *   cores (products exact, float64 rounding only). */
+#define DION_GRAM_F64     0x400
 
 /* Row-sharded step (FSDP layout; the sharded setting the Dion and
  * Orth-Dion abstracts motivate).  OR DION_SHARDED into the variant of

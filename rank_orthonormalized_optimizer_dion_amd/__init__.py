@@ -31,6 +31,7 @@ ERR_BREAKDOWN = -4
 VARIANTS = {"dion": 0, "orth": 1}
 MATH = {"f32": 0x000, "bf16x3": 0x100}
 SHARDED = 0x200
+GRAM_F64 = 0x400   # OR into math: float64 MFMA Gram matrix instead of sliced int8
 SHARD_GRAM, SHARD_W = 0, 1
 STATUS_ORTH_P, STATUS_ORTH_W, STATUS_COLNORM = 1, 2, 4
 

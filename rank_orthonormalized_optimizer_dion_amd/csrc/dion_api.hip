@@ -68,6 +68,7 @@ struct ClassRec {
 struct dion_plan {
   int count = 0, variant = 0, gdtype = 0;
   int math = 0;                       // 0: float32 MFMA, 1: split-bfloat16
+  bool gram8 = true;                  // sliced int8 Gram (else float64 MFMA)
   bool sharded = false;               // DION_SHARDED: staged step with exchanges
   bool vec = false;
   bool single = false;
@@ -134,7 +135,8 @@ void pick_split(int64_t tiles, int K, int& s, int& klen) {
 int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool single,
                dion_plan& p) {
   if (!mats || count < 1) return DION_ERR_INVALID_ARG;
-  if (variant & ~(DION_VARIANT_MASK | DION_MATH_MASK | DION_SHARDED)) return DION_ERR_INVALID_ARG;
+  if (variant & ~(DION_VARIANT_MASK | DION_MATH_MASK | DION_SHARDED | DION_GRAM_F64))
+    return DION_ERR_INVALID_ARG;
   if ((variant & DION_SHARDED) && single) return DION_ERR_INVALID_ARG;
   const int rule = variant & DION_VARIANT_MASK;
   if (rule != DION_VARIANT_DION && rule != DION_VARIANT_ORTH) return DION_ERR_INVALID_ARG;
@@ -143,6 +145,7 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
   p.variant = rule;
   p.math = (variant & DION_MATH_BF16X3) ? 1 : 0;
   p.sharded = (variant & DION_SHARDED) != 0;
+  p.gram8 = (variant & DION_GRAM_F64) == 0;
   p.gdtype = gdtype;
   p.single = single;
   p.vec = true;
@@ -172,7 +175,8 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
       // most nt / (nt + 1) of the float64 matrix rate; 64-wide tiles halve
       // that loss and balance the grid better (r = 768: 1.5 ms less per
       // Gram than 128-wide tiles).
-      k.bg = k.r > 1024 ? pick_bn(k.r) : 64;
+      // (The sliced Gram always works on 64-wide tiles.)
+      k.bg = k.r > 1024 && !p.gram8 ? pick_bn(k.r) : 64;
       const bool big_r = k.r * 10 >= cdiv(k.r, 256) * 256 * 9;   // <= 10% of 256-wide tiles idle
       k.bn_mv = p.math && k.m >= 256 && big_r ? 256 : k.bn_r;
       k.bn_mtu = p.math && k.n >= 256 && big_r ? 256 : k.bn_r;
@@ -255,6 +259,7 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     d.oK = kpart ? take(kpart * 4) : 0;
     d.oH = p.math ? take(r * std::max(plane_pitch(k.m), plane_pitch(k.n)) * 4) : 0;
     d.oE = k.bn_n == 256 ? take((m + 2 * n) * plane_pitch(k.r) * 4) : 0;
+    d.oQ = p.gram8 ? take(static_cast<size_t>(q_bytes(std::max(k.m, k.n), k.r))) : 0;
     p.table[g] = d;
   }
   p.ws_bytes = off;
@@ -294,13 +299,42 @@ hipError_t grouped(const dion_plan& p, const Launch& base, Fill fill, Go go) {
   } while (0)
 
 // orth() of the P (which = 0) or W (which = 1) factor by one CholeskyQR
-// pass with a float64 Gram matrix: S = Q^T Q (float64 MFMA), S = T^T T and
+// pass with a float64 Gram matrix: S = Q^T Q (sliced int8 MFMA products,
+// or float64 MFMA with DION_GRAM_F64), S = T^T T and
 // Y = T^{-T} (float64, blocked), Q T^{-1} (float32 MFMA) into U (oB) or V.
 // gram() writes the Gram partials into oS; factor() does the rest.
 hipError_t gram(const dion_plan& p, Launch base, int which, hipStream_t st) {
   base.which = which;
   base.pass = 1;
   base.flag = which == 0 ? DION_STATUS_ORTH_P : DION_STATUS_ORTH_W;
+  if (p.gram8) {
+    // column maxima over row slices, digit planes, int8 digit products
+    auto qsplit = [&](const ClassRec& c, ClassInfo& ci) {
+      const int rows = which == 0 ? c.m : c.n;
+      ci.splits = std::min(kQMaxSplits, std::max(1, cdiv(rows, kQMaxRows)));
+      ci.klen = cdiv(rows, ci.splits);
+      ci.splits = cdiv(rows, ci.klen);
+      return rows;
+    };
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      qsplit(c, ci);
+      ci.tiles = ci.splits * cdiv(c.r, 64);
+      return true;
+    }, [&](const Launch& L) { return launch_qmax(L, st); }));
+    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      const int rows = qsplit(c, ci);
+      ci.tiles = static_cast<int>(q_cols(c.r) / 32) * cdiv(q_rows(rows) / 32, 4);
+      return true;
+    }, [&](const Launch& L) { return launch_qslice(L, st); }));
+    return grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      const int nt = cdiv(c.r, 64);
+      ci.tx = nt;
+      ci.splits = which == 0 ? c.s_gp : c.s_gw;
+      ci.klen = which == 0 ? c.kl_gp : c.kl_gw;
+      ci.tiles = nt * (nt + 1) / 2 * ci.splits;
+      return true;
+    }, [&](const Launch& L) { return launch_gram8(L, st); });
+  }
   for (int bg : {128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bg != bg) return false;

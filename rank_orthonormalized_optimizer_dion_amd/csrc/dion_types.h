@@ -13,6 +13,31 @@ inline __host__ __device__ int plane_pitch(int rows) { return (rows + kPlaneK - 
 // Grouped launches carry at most this many shape classes.
 constexpr int kMaxClasses = 8;
 
+// Sliced Gram matrix.  Each column of the factor Q is scaled by a power of
+// two 2^-e into (-1, 1) and written as kQDigits signed base-2^7 digits
+// (int8 values in [-64, 64]): q = 2^e sum_t d_t 2^-(7 t + 6), with a
+// remainder below 2^(e - 35).  The digits sit in fragment planes: plane t,
+// 32-column block cb, 32-row block kb is one 1 KB fragment whose lane
+// c + 32 h (16 bytes) holds rows 16 h .. 16 h + 15 of column c, the operand
+// order of the 32 x 32 x 32 int8 MFMA.  Rows and columns past the factor
+// are zero digits.  After the planes: per-slice column maxima (kQMaxSplits
+// x qcols uint32, the bits of max |q|) and the column exponents (qcols
+// int32), qcols = r rounded up to 32.
+constexpr int kQDigits = 5;
+constexpr int kQMaxSplits = 64;
+constexpr int kQMaxRows = 1024;      // fewest rows per column-maximum slice
+constexpr int kQBadExp = 1 << 30;    // exponent of a column with a non-finite entry
+inline __host__ __device__ int64_t q_cols(int r) { return (r + 31) / 32 * 32; }
+inline __host__ __device__ int64_t q_rows(int rows) { return (static_cast<int64_t>(rows) + 31) / 32 * 32; }
+// byte offsets inside the region, for factors of at most `rows_max` rows
+inline __host__ __device__ int64_t q_max_off(int rows_max, int r) {
+  return kQDigits * q_cols(r) * q_rows(rows_max);
+}
+inline __host__ __device__ int64_t q_exp_off(int rows_max, int r) {
+  return q_max_off(rows_max, r) + kQMaxSplits * q_cols(r) * 4;
+}
+inline __host__ __device__ int64_t q_bytes(int rows_max, int r) { return q_exp_off(rows_max, r) + q_cols(r) * 4; }
+
 // One matrix as the kernels see it.  Workspace offsets are bytes from the
 // workspace base.  rp = r rounded up to kCholNB.
 struct MatDesc {
@@ -40,6 +65,9 @@ struct MatDesc {
                      // bfloat16 each in plane_cell_r order (cell = 8
                      // consecutive rows of V or U), zero past the last row;
                      // 0 without them
+  int64_t oQ;        // sliced Gram: digit planes, column maxima and
+                     // exponents of the factor being orthogonalized
+                     // (layout above, rows_max = max(m, n)); 0 if unused
 };
 
 // Matrices with the same (m, n, r) form a class; inside one launch every

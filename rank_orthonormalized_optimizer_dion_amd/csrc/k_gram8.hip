@@ -1,0 +1,273 @@
+// Gram matrix S = Q^T Q of a CholeskyQR pass (orth() of the Orth-Dion
+// page's equations 2 and 4) on the int8 matrix cores.
+//
+// A float32 column q_j scaled by 2^-e_j (the power of two just above
+// max |q_j|) is a sum of kQDigits signed base-2^7 digits plus a remainder
+// below 2^-35:  q_j = 2^e_j sum_t d_jt 2^-(7 t + 6).  Then
+//   S_ij = 2^(e_i + e_j) sum_l 2^-(7 l + 12) sum_{a + b = l} D_ia . D_jb
+// and every digit product sum D_ia . D_jb is an integer, summed exactly by
+// the int32 accumulation of v_mfma_i32_32x32x32_i8.  Keeping the levels
+// l <= kQDigits - 1 (15 digit products) leaves an error of order
+// 2^-34 |q_i|_max |q_j|_1 per entry, a relative error near 1e-11 for columns
+// of a few thousand entries: far below what one CholeskyQR pass needs
+// (the float64 Gram kernel's result agrees to the same order).  Each level's
+// int32 sum is moved to float64 every kQFlushSteps steps, before it could
+// overflow.
+//
+//   k_qmax    max |q_j| over row slices, as float bits (a non-finite entry
+//             gives a maximum at or above the bits of +inf)
+//   k_qslice  column exponents and the digit planes
+//   k_gram8   upper-triangle 64 x 64 tiles of S from the digit planes
+#include <math.h>
+
+#include "device_common.h"
+#include "launchers.h"
+
+namespace dion {
+
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// 2048 steps of 32 rows: a level adds at most kQDigits products of digits
+// of magnitude <= 64 per row, 65536 * 5 * 4096 < 2^31.
+constexpr int kQFlushSteps = 2048;
+
+__device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
+  return L.status[d.slot] != 0;
+}
+
+__device__ __forceinline__ const float* q_source(const Launch& L, const MatDesc& d) {
+  return reinterpret_cast<const float*>(L.ws + (L.which == 0 ? d.oP : d.oW));
+}
+
+__device__ __forceinline__ int rows_max(const MatDesc& d) { return d.m > d.n ? d.m : d.n; }
+
+// Work item (slice sp, 64-column group cg): the largest |q| bit pattern of
+// each column over rows [sp klen, (sp + 1) klen), 4 row groups combined
+// through LDS.
+__global__ __launch_bounds__(kThreads) void k_qmax(Launch L) {
+  __shared__ uint32_t red[4][64];
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int rows = L.which == 0 ? d.m : d.n;
+  const int groups = (d.r + 63) / 64;
+  const int sp = local / groups, cg = local - sp * groups;
+  gptr<const uint32_t> Q = to_global(reinterpret_cast<const uint32_t*>(q_source(L, d)));
+  const int col = cg * 64 + (threadIdx.x & 63);
+  const int rg = threadIdx.x >> 6;
+  const int i0 = sp * ci.klen, i1 = min(rows, i0 + ci.klen);
+  uint32_t mx = 0;
+  if (col < d.r) {
+    // 8 rows per round, issued together: rows past the slice repeat its
+    // last row, which does not change the maximum
+    for (int i = i0 + rg; i < i1; i += 32) {
+      uint32_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = Q[static_cast<int64_t>(min(i + 4 * j, i1 - 1)) * d.r + col];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = max(mx, v[j] & 0x7fffffffu);
+    }
+  }
+  red[rg][threadIdx.x & 63] = mx;
+  __syncthreads();
+  if (rg == 0 && col < d.r) {
+    uint32_t* part = reinterpret_cast<uint32_t*>(L.ws + d.oQ + q_max_off(rows_max(d), d.r));
+    part[static_cast<int64_t>(sp) * q_cols(d.r) + col] =
+        max(max(red[0][threadIdx.x], red[1][threadIdx.x]), max(red[2][threadIdx.x], red[3][threadIdx.x]));
+  }
+}
+
+// Work item (32-column block cb, group kq of 4 row blocks); wavefront w
+// writes fragment (cb, 4 kq + w) of every digit plane.  Lane c + 32 h takes
+// rows 16 h .. 16 h + 15 of column 32 cb + c.
+__global__ __launch_bounds__(kThreads) void k_qslice(Launch L) {
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int rows = L.which == 0 ? d.m : d.n;
+  const int ncb = static_cast<int>(q_cols(d.r) / 32), nkb = static_cast<int>(q_rows(rows) / 32);
+  const int nkq = (nkb + 3) / 4;
+  const int cb = local / nkq;
+  const int kb = (local - cb * nkq) * 4 + (threadIdx.x >> 6);
+  if (kb >= nkb) return;
+  const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
+  const int col = cb * 32 + c;
+  const int rmax = rows_max(d);
+  const char* region = L.ws + d.oQ;
+  // Loads below use in-range indices (clamped) and discard what lies
+  // outside, so that each group of them is issued at once.
+  const int colc = min(col, d.r - 1);
+  uint32_t mx = 0;
+  {
+    gptr<const uint32_t> part = to_global(reinterpret_cast<const uint32_t*>(region + q_max_off(rmax, d.r)));
+    for (int sp = 0; sp < ci.splits; sp += 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = part[static_cast<int64_t>(min(sp + j, ci.splits - 1)) * q_cols(d.r) + colc];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = max(mx, v[j]);
+    }
+    if (col >= d.r) mx = 0;
+  }
+  const bool bad = mx >= 0x7f800000u;
+  int e = 0;
+  if (!bad && mx != 0) frexpf(__uint_as_float(mx), &e);   // max |q| < 2^e
+  if (kb == 0 && h == 0)
+    reinterpret_cast<int*>(L.ws + d.oQ + q_exp_off(rmax, d.r))[col] = bad ? kQBadExp : e;
+  const double scale = ldexp(1.0, -e);
+  gptr<const float> Q = to_global(q_source(L, d));
+  uint32_t w[kQDigits][4];
+#pragma unroll
+  for (int t = 0; t < kQDigits; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[t][j] = 0;
+  const bool live = col < d.r && !bad;
+  float qv[16];
+#pragma unroll
+  for (int b = 0; b < 16; ++b) qv[b] = Q[static_cast<int64_t>(min(kb * 32 + 16 * h + b, rows - 1)) * d.r + colc];
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    const int row = kb * 32 + 16 * h + b;
+    const float q = live && row < rows ? qv[b] : 0.0f;
+    // |y| < 1; every step below is exact in float64 (y keeps at most the
+    // 24 significant bits of q)
+    double y = static_cast<double>(q) * scale;
+#pragma unroll
+    for (int t = 0; t < kQDigits; ++t) {
+      const double up = ldexp(1.0, 7 * t + 6), down = ldexp(1.0, -(7 * t + 6));
+      const double x = rint(y * up);   // |x| <= 64
+      y -= x * down;
+      w[t][b >> 2] |= (static_cast<uint32_t>(static_cast<int>(x)) & 0xffu) << (8 * (b & 3));
+    }
+  }
+  gptr<u32x4> planes = to_global(reinterpret_cast<u32x4*>(L.ws + d.oQ));
+  const int64_t frag = (static_cast<int64_t>(cb) * nkb + kb) * 64 + lane;
+  const int64_t tstride = static_cast<int64_t>(ncb) * nkb * 64;
+#pragma unroll
+  for (int t = 0; t < kQDigits; ++t) planes[t * tstride + frag] = u32x4{w[t][0], w[t][1], w[t][2], w[t][3]};
+}
+
+__device__ __forceinline__ void load_frags(gptr<const i32x4> pa, gptr<const i32x4> pb, int64_t tstride,
+                                           int kb, i32x4 (&a)[kQDigits], i32x4 (&b)[kQDigits]) {
+#pragma unroll
+  for (int t = 0; t < kQDigits; ++t) {
+    a[t] = pa[t * tstride + kb * 64];
+    b[t] = pb[t * tstride + kb * 64];
+  }
+}
+
+// acc[l] += sum over digit pairs a + b = l of D_a^T D_b (15 MFMAs).
+__device__ __forceinline__ void digit_products(const i32x4 (&a)[kQDigits], const i32x4 (&b)[kQDigits],
+                                               i32x16 (&acc)[kQDigits]) {
+#pragma unroll
+  for (int l = 0; l < kQDigits; ++l)
+#pragma unroll
+    for (int ta = 0; ta <= l; ++ta)
+      acc[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ta], b[l - ta], acc[l], 0, 0, 0);
+}
+
+// Partial Gram matrix S_s = Q[kbeg:kend]^T Q[kbeg:kend] on 64 x 64 upper-
+// triangle tiles: four wavefronts of 32 x 32, each loading its own digit
+// fragments straight into registers one step ahead (no LDS).  On a diagonal
+// tile the wavefront of rows 32.. and columns ..32 lies below the diagonal
+// and does nothing (the factorization reads the upper triangle only).
+// Two blocks per CU (at most 256 registers per lane).
+__global__ __launch_bounds__(kThreads, 2) void k_gram8(Launch L) {
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int rows = L.which == 0 ? d.m : d.n;
+  const int nt = ci.tx;
+  const int pairs = nt * (nt + 1) / 2;
+  const int s = local / pairs;
+  int p = local - s * pairs;
+  int ti = 0;
+  while (p >= nt - ti) {
+    p -= nt - ti;
+    ++ti;
+  }
+  const int tj = ti + p;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (ti == tj && wm > wn) return;
+  const int ncb = static_cast<int>(q_cols(d.r) / 32), nkb = static_cast<int>(q_rows(rows) / 32);
+  const int cba = ti * 2 + wm, cbb = tj * 2 + wn;   // cba <= cbb
+  if (cbb >= ncb) return;
+  const int kbeg = s * ci.klen;
+  const int kend = min(rows, kbeg + ci.klen);
+  if (kend <= kbeg) return;
+  const int kb0 = kbeg / 32, kb1 = (kend + 31) / 32;
+  const int64_t tstride = static_cast<int64_t>(ncb) * nkb * 64;
+  gptr<const i32x4> planes = to_global(reinterpret_cast<const i32x4*>(L.ws + d.oQ));
+  gptr<const i32x4> pa = planes + static_cast<int64_t>(cba) * nkb * 64 + lane;
+  gptr<const i32x4> pb = planes + static_cast<int64_t>(cbb) * nkb * 64 + lane;
+  double sum[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) sum[v] = 0.0;
+  i32x4 a[kQDigits], b[kQDigits];
+  load_frags(pa, pb, tstride, kb0, a, b);
+  for (int c0 = kb0; c0 < kb1; c0 += kQFlushSteps) {
+    const int c1 = min(kb1, c0 + kQFlushSteps);
+    i32x16 acc[kQDigits];
+#pragma unroll
+    for (int l = 0; l < kQDigits; ++l)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[l][v] = 0;
+    for (int kb = c0; kb < c1; ++kb) {
+      i32x4 an[kQDigits], bn[kQDigits];
+      load_frags(pa, pb, tstride, min(kb + 1, kb1 - 1), an, bn);   // the last step reloads itself
+      digit_products(a, b, acc);
+#pragma unroll
+      for (int t = 0; t < kQDigits; ++t) {
+        a[t] = an[t];
+        b[t] = bn[t];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      double x = 0.0;
+#pragma unroll
+      for (int l = kQDigits - 1; l >= 0; --l) x += ldexp(static_cast<double>(acc[l][v]), -(7 * l + 12));
+      sum[v] += x;
+    }
+  }
+  const int* qexp = reinterpret_cast<const int*>(L.ws + d.oQ + q_exp_off(rows_max(d), d.r));
+  gptr<double> out = to_global(reinterpret_cast<double*>(L.ws + d.oS) + static_cast<int64_t>(s) * d.rp * d.rp);
+  const int col = cbb * 32 + (lane & 31);
+  if (col >= d.r) return;
+  const int ej = qexp[col];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    // 32 x 32 MFMA result: lane l, register v holds row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
+    const int row = cba * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    if (row < d.r) {
+      const int ei = qexp[row];
+      out[static_cast<int64_t>(row) * d.rp + col] =
+          ei == kQBadExp || ej == kQBadExp ? __builtin_nan("") : ldexp(sum[v], ei + ej);
+    }
+  }
+}
+
+template <class K>
+hipError_t go(K kernel, const Launch& L, hipStream_t st) {
+  if (L.total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(L.total), dim3(kThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qmax(const Launch& L, hipStream_t st) { return go(k_qmax, L, st); }
+hipError_t launch_qslice(const Launch& L, hipStream_t st) { return go(k_qslice, L, st); }
+hipError_t launch_gram8(const Launch& L, hipStream_t st) { return go(k_gram8, L, st); }
+
+}  // namespace dion

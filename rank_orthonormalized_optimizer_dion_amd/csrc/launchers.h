@@ -14,6 +14,10 @@ namespace dion {
 hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st);
 hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st);
 hipError_t launch_gram(const Launch& L, int bg, bool vec, hipStream_t st);
+// Sliced Gram matrix: column maxima, digit planes, int8 MFMA products.
+hipError_t launch_qmax(const Launch& L, hipStream_t st);
+hipError_t launch_qslice(const Launch& L, hipStream_t st);
+hipError_t launch_gram8(const Launch& L, hipStream_t st);
 // math = 1: three-way split bfloat16 products of float32 accuracy (k_trmm6)
 hipError_t launch_trmm(const Launch& L, int bn, bool vec, int math, hipStream_t st);
 hipError_t launch_epi(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st);

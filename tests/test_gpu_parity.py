@@ -94,6 +94,22 @@ def test_config2_one_step(gpu_lib, variant, arith):
     assert_close(c.errors(x_prev), TOL_1, f"config2 {variant}")
 
 
+@pytest.mark.parametrize("variant", [ORTH, DION])
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+@pytest.mark.parametrize("wl_shape", ["config2", "ragged"])
+def test_float64_gram_option(gpu_lib, variant, arith, wl_shape):
+    # DION_GRAM_F64: the Gram matrix on the float64 matrix cores instead of
+    # the sliced int8 products (the default everywhere else in this file)
+    wl = config(2) if wl_shape == "config2" else _wl(400, 300, 150)
+    c = Case(wl, wl.mats[0])
+    c.load_grad(0)
+    say(f"{wl_shape} {variant} {arith} float64 Gram one step")
+    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant,
+                 math=gpu_lib.MATH[arith] | gpu_lib.GRAM_F64)
+    _, x_prev = c.oracle(variant)
+    assert_close(c.errors(x_prev), TOL_1, f"{wl_shape} {variant} float64 Gram")
+
+
 @pytest.mark.parametrize("arith", ["f32", "bf16x3"])
 def test_config5_r512_one_step(gpu_lib, arith):
     wl = config(5, r=512)
