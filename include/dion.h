@@ -84,13 +84,15 @@ extern "C" {
 
 /* Gram matrix S = Q^T Q of orth()'s CholeskyQR pass (orth() of equations 2
  * and 4 of the Orth-Dion page), OR-ed into `variant` like the math mode.
- * Default: each float32 column of Q is scaled by a power of two into
+ * Default: each float32 column q_j of Q is scaled by a power of two into
  *   (-1, 1) and written as five signed base-128 digits (int8); S is
  *   assembled in float64 from the 15 leading digit products, each summed
- *   exactly in int32 on the int8 matrix cores.  Entry error about
- *   2^-34 max|q_i| sum|q_j|, i.e. near 1e-11 relative for columns of a few
- *   thousand entries; a non-finite entry of Q makes its row and column of S
- *   NaN (a breakdown of the factorization).
+ *   exactly in int32 on the int8 matrix cores.  Each product q_ik q_jk
+ *   enters S with an error below 2^-30 max|q_i| max|q_j| (the digits'
+ *   remainder and the dropped digit products); over many rows these errors
+ *   add like independent roundings (measured: Gram entries within 2e-10 of
+ *   sqrt(S_ii S_jj) of the float64 Gram).  A non-finite entry of Q makes
+ *   its row and column of S NaN, a breakdown of the factorization.
  * DION_GRAM_F64: float32 products summed in float64 on the float64 matrix
  *   cores (products exact, float64 rounding only). */
 #define DION_GRAM_F64     0x400

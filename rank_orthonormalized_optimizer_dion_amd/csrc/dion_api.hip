@@ -318,12 +318,12 @@ hipError_t gram(const dion_plan& p, Launch base, int which, hipStream_t st) {
     };
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       qsplit(c, ci);
-      ci.tiles = ci.splits * cdiv(c.r, 64);
+      ci.tiles = ci.splits * cdiv(c.r, 256);
       return true;
     }, [&](const Launch& L) { return launch_qmax(L, st); }));
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       const int rows = qsplit(c, ci);
-      ci.tiles = static_cast<int>(q_cols(c.r) / 32) * cdiv(q_rows(rows) / 32, 4);
+      ci.tiles = static_cast<int>(q_rows(rows) / 32) * cdiv(q_cols(c.r) / 32, 4);
       return true;
     }, [&](const Launch& L) { return launch_qslice(L, st); }));
     return grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {

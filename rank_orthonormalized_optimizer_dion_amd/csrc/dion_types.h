@@ -25,7 +25,7 @@ constexpr int kMaxClasses = 8;
 // int32), qcols = r rounded up to 32.
 constexpr int kQDigits = 5;
 constexpr int kQMaxSplits = 64;
-constexpr int kQMaxRows = 1024;      // fewest rows per column-maximum slice
+constexpr int kQMaxRows = 256;       // fewest rows per column-maximum slice
 constexpr int kQBadExp = 1 << 30;    // exponent of a column with a non-finite entry
 inline __host__ __device__ int64_t q_cols(int r) { return (r + 31) / 32 * 32; }
 inline __host__ __device__ int64_t q_rows(int rows) { return (static_cast<int64_t>(rows) + 31) / 32 * 32; }

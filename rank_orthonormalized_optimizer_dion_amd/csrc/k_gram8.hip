@@ -7,12 +7,15 @@
 //   S_ij = 2^(e_i + e_j) sum_l 2^-(7 l + 12) sum_{a + b = l} D_ia . D_jb
 // and every digit product sum D_ia . D_jb is an integer, summed exactly by
 // the int32 accumulation of v_mfma_i32_32x32x32_i8.  Keeping the levels
-// l <= kQDigits - 1 (15 digit products) leaves an error of order
-// 2^-34 |q_i|_max |q_j|_1 per entry, a relative error near 1e-11 for columns
-// of a few thousand entries: far below what one CholeskyQR pass needs
-// (the float64 Gram kernel's result agrees to the same order).  Each level's
-// int32 sum is moved to float64 every kQFlushSteps steps, before it could
-// overflow.
+// l <= kQDigits - 1 (15 digit products) forms each product q_ik q_jk to
+// within 2^-30 max|q_i| max|q_j|: the terms d_a 2^-(7 a + 6) with a >= 1 are
+// at most 2^-7a in size, so the dropped products (a + b >= kQDigits) and the remainders
+// of the two columns add up to about 6 2^-35 in units of 2^(e_i + e_j) <=
+// 4 max|q_i| max|q_j|.  Those errors come from rounding each entry to
+// digits and add like independent roundings over the rows.  The levels
+// are combined exactly in int64 and rounded once to float64; each level's
+// int32 sum is moved out (added into the output) every kQFlushSteps steps,
+// before it could overflow.
 //
 //   k_qmax    max |q_j| over row slices, as float bits (a non-finite entry
 //             gives a maximum at or above the bits of +inf)
@@ -44,47 +47,56 @@ __device__ __forceinline__ const float* q_source(const Launch& L, const MatDesc&
 
 __device__ __forceinline__ int rows_max(const MatDesc& d) { return d.m > d.n ? d.m : d.n; }
 
-// Work item (slice sp, 64-column group cg): the largest |q| bit pattern of
-// each column over rows [sp klen, (sp + 1) klen), 4 row groups combined
-// through LDS.
+// Work item (slice sp, 256-column group cg): the largest |q| bit pattern
+// of each column over rows [sp klen, (sp + 1) klen).  Wavefront w takes
+// rows w, w + 4, ..., lane l columns 256 cg + l + 64 j (j < 4), 8 rows per
+// round with all 32 loads issued together (indices clamped into the matrix:
+// a repeated row or column does not change a maximum, and columns past r
+// are not stored); the 4 wavefronts combine through LDS.
 __global__ __launch_bounds__(kThreads) void k_qmax(Launch L) {
-  __shared__ uint32_t red[4][64];
+  __shared__ uint32_t red[4][256];
   MatDesc d;
   ClassInfo ci;
   int local;
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
   const int rows = L.which == 0 ? d.m : d.n;
-  const int groups = (d.r + 63) / 64;
+  const int groups = (d.r + 255) / 256;
   const int sp = local / groups, cg = local - sp * groups;
   gptr<const uint32_t> Q = to_global(reinterpret_cast<const uint32_t*>(q_source(L, d)));
-  const int col = cg * 64 + (threadIdx.x & 63);
-  const int rg = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  int cc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cc[j] = min(cg * 256 + lane + 64 * j, d.r - 1);
   const int i0 = sp * ci.klen, i1 = min(rows, i0 + ci.klen);
-  uint32_t mx = 0;
-  if (col < d.r) {
-    // 8 rows per round, issued together: rows past the slice repeat its
-    // last row, which does not change the maximum
-    for (int i = i0 + rg; i < i1; i += 32) {
-      uint32_t v[8];
+  uint32_t mx[4] = {0, 0, 0, 0};
+  for (int i = i0 + rg; i < i1; i += 32) {
+    uint32_t v[8][4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = Q[static_cast<int64_t>(min(i + 4 * j, i1 - 1)) * d.r + col];
+    for (int k = 0; k < 8; ++k) {
+      const int64_t row = static_cast<int64_t>(min(i + 4 * k, i1 - 1)) * d.r;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mx = max(mx, v[j] & 0x7fffffffu);
+      for (int j = 0; j < 4; ++j) v[k][j] = Q[row + cc[j]];
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx[j] = max(mx[j], v[k][j] & 0x7fffffffu);
   }
-  red[rg][threadIdx.x & 63] = mx;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[rg][lane + 64 * j] = mx[j];
   __syncthreads();
-  if (rg == 0 && col < d.r) {
+  const int c = threadIdx.x, col = cg * 256 + c;
+  if (col < d.r) {
     uint32_t* part = reinterpret_cast<uint32_t*>(L.ws + d.oQ + q_max_off(rows_max(d), d.r));
-    part[static_cast<int64_t>(sp) * q_cols(d.r) + col] =
-        max(max(red[0][threadIdx.x], red[1][threadIdx.x]), max(red[2][threadIdx.x], red[3][threadIdx.x]));
+    part[static_cast<int64_t>(sp) * q_cols(d.r) + col] = max(max(red[0][c], red[1][c]), max(red[2][c], red[3][c]));
   }
 }
 
-// Work item (32-column block cb, group kq of 4 row blocks); wavefront w
-// writes fragment (cb, 4 kq + w) of every digit plane.  Lane c + 32 h takes
-// rows 16 h .. 16 h + 15 of column 32 cb + c.
+// Work item (32-row block kb, group cg of 4 column blocks); wavefront w
+// writes fragment (4 cg + w, kb) of every digit plane.  Lane c + 32 h takes
+// rows 16 h .. 16 h + 15 of column 32 (4 cg + w) + c.  Consecutive work
+// items read consecutive 512-byte spans of the same 32 rows.
 __global__ __launch_bounds__(kThreads) void k_qslice(Launch L) {
   MatDesc d;
   ClassInfo ci;
@@ -93,10 +105,10 @@ __global__ __launch_bounds__(kThreads) void k_qslice(Launch L) {
   if (skipped(L, d)) return;
   const int rows = L.which == 0 ? d.m : d.n;
   const int ncb = static_cast<int>(q_cols(d.r) / 32), nkb = static_cast<int>(q_rows(rows) / 32);
-  const int nkq = (nkb + 3) / 4;
-  const int cb = local / nkq;
-  const int kb = (local - cb * nkq) * 4 + (threadIdx.x >> 6);
-  if (kb >= nkb) return;
+  const int ncg = (ncb + 3) / 4;
+  const int kb = local / ncg;
+  const int cb = (local - kb * ncg) * 4 + (threadIdx.x >> 6);
+  if (cb >= ncb) return;
   const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
   const int col = cb * 32 + c;
   const int rmax = rows_max(d);
@@ -172,10 +184,19 @@ __device__ __forceinline__ void digit_products(const i32x4 (&a)[kQDigits], const
     for (int ta = 0; ta <= l; ++ta)
       acc[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ta], b[l - ta], acc[l], 0, 0, 0);
 }
+// The levels of one result entry, sum_l acc[l] 2^-(7 l + 12), combined
+// exactly in int64 (|acc[l]| < 2^31, so the sum stays below 2^62) and
+// rounded once to float64.
+__device__ __forceinline__ double level_sum(const i32x16 (&acc)[kQDigits], int v) {
+  int64_t x = 0;
+#pragma unroll
+  for (int l = 0; l < kQDigits; ++l) x += static_cast<int64_t>(acc[l][v]) << (7 * (kQDigits - 1 - l));
+  return ldexp(static_cast<double>(x), -(7 * (kQDigits - 1) + 12));
+}
 
 // Partial Gram matrix S_s = Q[kbeg:kend]^T Q[kbeg:kend] on 64 x 64 upper-
 // triangle tiles: four wavefronts of 32 x 32, each loading its own digit
-// fragments straight into registers one step ahead (no LDS).  On a diagonal
+// fragments straight into registers two steps ahead (no LDS).  On a diagonal
 // tile the wavefront of rows 32.. and columns ..32 lies below the diagonal
 // and does nothing (the factorization reads the upper triangle only).
 // Two blocks per CU (at most 256 registers per lane).
@@ -210,11 +231,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_gram8(Launch L) {
   gptr<const i32x4> planes = to_global(reinterpret_cast<const i32x4*>(L.ws + d.oQ));
   gptr<const i32x4> pa = planes + static_cast<int64_t>(cba) * nkb * 64 + lane;
   gptr<const i32x4> pb = planes + static_cast<int64_t>(cbb) * nkb * 64 + lane;
-  double sum[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) sum[v] = 0.0;
-  i32x4 a[kQDigits], b[kQDigits];
+  const int* qexp = reinterpret_cast<const int*>(L.ws + d.oQ + q_exp_off(rows_max(d), d.r));
+  gptr<double> out = to_global(reinterpret_cast<double*>(L.ws + d.oS) + static_cast<int64_t>(s) * d.rp * d.rp);
+  const int col = cbb * 32 + (lane & 31);
+  const int ej = qexp[min(col, d.r - 1)];
+  i32x4 a[kQDigits], b[kQDigits], a1[kQDigits], b1[kQDigits];
   load_frags(pa, pb, tstride, kb0, a, b);
+  load_frags(pa, pb, tstride, min(kb0 + 1, kb1 - 1), a1, b1);
   for (int c0 = kb0; c0 < kb1; c0 += kQFlushSteps) {
     const int c1 = min(kb1, c0 + kQFlushSteps);
     i32x16 acc[kQDigits];
@@ -224,35 +247,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_gram8(Launch L) {
       for (int v = 0; v < 16; ++v) acc[l][v] = 0;
     for (int kb = c0; kb < c1; ++kb) {
       i32x4 an[kQDigits], bn[kQDigits];
-      load_frags(pa, pb, tstride, min(kb + 1, kb1 - 1), an, bn);   // the last step reloads itself
+      load_frags(pa, pb, tstride, min(kb + 2, kb1 - 1), an, bn);   // the last steps reload the last
       digit_products(a, b, acc);
 #pragma unroll
       for (int t = 0; t < kQDigits; ++t) {
-        a[t] = an[t];
-        b[t] = bn[t];
+        a[t] = a1[t];
+        b[t] = b1[t];
+        a1[t] = an[t];
+        b1[t] = bn[t];
       }
     }
+    // this interval's share of S, into the tile's own entries of S_s
+    // (written by the first interval, added to by later ones)
+    if (col < d.r) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      double x = 0.0;
-#pragma unroll
-      for (int l = kQDigits - 1; l >= 0; --l) x += ldexp(static_cast<double>(acc[l][v]), -(7 * l + 12));
-      sum[v] += x;
-    }
-  }
-  const int* qexp = reinterpret_cast<const int*>(L.ws + d.oQ + q_exp_off(rows_max(d), d.r));
-  gptr<double> out = to_global(reinterpret_cast<double*>(L.ws + d.oS) + static_cast<int64_t>(s) * d.rp * d.rp);
-  const int col = cbb * 32 + (lane & 31);
-  if (col >= d.r) return;
-  const int ej = qexp[col];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    // 32 x 32 MFMA result: lane l, register v holds row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
-    const int row = cba * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    if (row < d.r) {
-      const int ei = qexp[row];
-      out[static_cast<int64_t>(row) * d.rp + col] =
-          ei == kQBadExp || ej == kQBadExp ? __builtin_nan("") : ldexp(sum[v], ei + ej);
+      for (int v = 0; v < 16; ++v) {
+        // 32 x 32 MFMA result: lane l, register v holds row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
+        const int row = cba * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < d.r) {
+          const int ei = qexp[row];
+          double x = level_sum(acc, v);
+          x = ei == kQBadExp || ej == kQBadExp ? __builtin_nan("") : ldexp(x, ei + ej);
+          const int64_t o = static_cast<int64_t>(row) * d.rp + col;
+          out[o] = c0 == kb0 ? x : out[o] + x;
+        }
+      }
     }
   }
 }

@@ -124,3 +124,14 @@ def test_shard_entry_points_reject_null_plan(lib):
         dion.ERR_INVALID_ARG
     assert lib.dion_plan_shard_buffer(None, 0, 0, ctypes.byref(off), ctypes.byref(nb)) == \
         dion.ERR_INVALID_ARG
+
+
+def test_gram_variant_bit(lib):
+    # the sliced Gram (default) needs its digit planes in the workspace;
+    # DION_GRAM_F64 does not, and an unknown bit is rejected
+    m, n, r = 3072, 8192, 768
+    sliced = lib.dion_workspace_size(m, n, r, 1, 1)
+    f64 = lib.dion_workspace_size(m, n, r, 1 | dion.GRAM_F64, 1)
+    assert f64 > 0
+    assert sliced - f64 >= 5 * r * max(m, n)
+    assert lib.dion_workspace_size(m, n, r, 1 | 0x800, 1) == 0
