@@ -133,7 +133,6 @@ __global__ __launch_bounds__(kThreads) void k_qslice(Launch L) {
   if (!bad && mx != 0) frexpf(__uint_as_float(mx), &e);   // max |q| < 2^e
   if (kb == 0 && h == 0)
     reinterpret_cast<int*>(L.ws + d.oQ + q_exp_off(rmax, d.r))[col] = bad ? kQBadExp : e;
-  const double scale = ldexp(1.0, -e);
   gptr<const float> Q = to_global(q_source(L, d));
   uint32_t w[kQDigits][4];
 #pragma unroll
@@ -148,13 +147,14 @@ __global__ __launch_bounds__(kThreads) void k_qslice(Launch L) {
   for (int b = 0; b < 16; ++b) {
     const int row = kb * 32 + 16 * h + b;
     const float q = live && row < rows ? qv[b] : 0.0f;
-    // |y| < 1; every step below is exact in float64 (y keeps at most the
-    // 24 significant bits of q)
-    double y = static_cast<double>(q) * scale;
+    // |y| < 1; every step below is exact in float32 (y keeps at most the
+    // 24 significant bits of q; a y below 2^-126 loses only bits far
+    // under the digits' reach)
+    float y = ldexpf(q, -e);
 #pragma unroll
     for (int t = 0; t < kQDigits; ++t) {
-      const double up = ldexp(1.0, 7 * t + 6), down = ldexp(1.0, -(7 * t + 6));
-      const double x = rint(y * up);   // |x| <= 64
+      const float up = ldexpf(1.0f, 7 * t + 6), down = ldexpf(1.0f, -(7 * t + 6));
+      const float x = rintf(y * up);   // |x| <= 64
       y -= x * down;
       w[t][b >> 2] |= (static_cast<uint32_t>(static_cast<int>(x)) & 0xffu) << (8 * (b & 3));
     }

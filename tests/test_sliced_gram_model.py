@@ -127,3 +127,20 @@ def test_model_detects_a_missing_level():
     finally:
         DIGITS = saved
     assert np.max(np.abs(S - E) / np.outer(d, d)) > 1e-9
+
+
+def test_float32_digit_steps_are_exact():
+    # the digit steps in float32 (scale by 2^-e, then per digit: multiply by
+    # a power of two, round to nearest, subtract) give the float64 digits,
+    # including entries far below the column's largest and subnormal ones
+    rng = np.random.default_rng(3)
+    q = (rng.standard_normal(20000) * np.exp(rng.uniform(-60, 0, 20000))).astype(np.float32)
+    q[:4] = np.array([1.0, -0.999999, 1e-40, -3e-42], dtype=np.float32)
+    e = column_exponent(q)
+    d64, _ = digits(q, e)
+    y = np.ldexp(q, -e).astype(np.float32)
+    for t in range(DIGITS):
+        up = np.float32(2.0 ** (7 * t + 6))
+        x = np.rint(y * up).astype(np.float32)
+        y = (y - x / up).astype(np.float32)
+        assert np.array_equal(x.astype(np.int64), d64[t]), t
