@@ -308,15 +308,28 @@ hipError_t gram(const dion_plan& p, Launch base, int which, hipStream_t st) {
   base.pass = 1;
   base.flag = which == 0 ? DION_STATUS_ORTH_P : DION_STATUS_ORTH_W;
   if (p.gram8) {
-    // column maxima over row slices, digit planes, int8 digit products
+    // column maxima over row slices (unless the kernel that wrote the
+    // factor left them: then one slice per 256-row tile), digit planes,
+    // int8 digit products.  A sharded plan's W is the caller's sum over
+    // the shards, so its maxima are taken afresh.
+    auto fused = [&](const ClassRec& c) {
+      return which == 0 ? c.bn_mv == 256 && q_fused_max(1, c.s_mv, cdiv(c.m, 256))
+                        : c.bn_mtu == 256 && !p.sharded && q_fused_max(1, c.s_mtu, cdiv(c.n, 256));
+    };
     auto qsplit = [&](const ClassRec& c, ClassInfo& ci) {
       const int rows = which == 0 ? c.m : c.n;
+      if (fused(c)) {
+        ci.splits = cdiv(rows, 256);
+        ci.klen = 256;
+        return rows;
+      }
       ci.splits = std::min(kQMaxSplits, std::max(1, cdiv(rows, kQMaxRows)));
       ci.klen = cdiv(rows, ci.splits);
       ci.splits = cdiv(rows, ci.klen);
       return rows;
     };
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+      if (fused(c)) return false;
       qsplit(c, ci);
       ci.tiles = ci.splits * cdiv(c.r, 256);
       return true;

@@ -37,6 +37,13 @@ inline __host__ __device__ int64_t q_exp_off(int rows_max, int r) {
   return q_max_off(rows_max, r) + kQMaxSplits * q_cols(r) * 4;
 }
 inline __host__ __device__ int64_t q_bytes(int rows_max, int r) { return q_exp_off(rows_max, r) + q_cols(r) * 4; }
+// The split-bfloat16 256 x 256 kernels that produce P (M V) and W (M^T U)
+// write the column maxima of each 256-row tile into slice `row tile` of the
+// maxima themselves when the region exists, the reduction is not split and
+// there are at most kQMaxSplits row tiles.
+inline __host__ __device__ bool q_fused_max(int64_t oQ, int splits, int row_tiles) {
+  return oQ != 0 && splits == 1 && row_tiles <= kQMaxSplits;
+}
 
 // One matrix as the kernels see it.  Workspace offsets are bytes from the
 // workspace base.  rp = r rounded up to kCholNB.

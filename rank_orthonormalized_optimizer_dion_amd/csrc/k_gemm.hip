@@ -578,6 +578,42 @@ __device__ __forceinline__ void store_tile_w(float* out_, int64_t ld, int r0, in
     }
 }
 
+// Column maxima of |acc| over the tile's rows below rmax, as float bits (a
+// non-finite entry gives at least the bits of +inf), into part[c0 + c] for
+// the columns below cmax: lanes, then lane halves, then the wavefront rows
+// through LDS.  Called by the whole block after the main loop's last
+// barrier, when LDS is free.
+template <class W>
+__device__ __forceinline__ void store_colmax(uint32_t* part_, int r0, int c0, int rmax, int cmax,
+                                             const f32x16 (&acc)[W::FM][W::FN], u32x4* smem) {
+  uint32_t* red = reinterpret_cast<uint32_t*>(smem);   // [GM][BN]
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int fn = 0; fn < W::FN; ++fn) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int fm = 0; fm < W::FM; ++fm)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (r0 + W::row(fm, v) < rmax) mx = max(mx, __float_as_uint(acc[fm][fn][v]) & 0x7fffffffu);
+    mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), 32)));
+    if (lane < 32) red[W::wm() * W::BN + W::col(fn)] = mx;
+  }
+  __syncthreads();
+  gptr<uint32_t> part = to_global(part_);
+  for (int c = threadIdx.x; c < W::BN; c += W::NT) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int g = 0; g < W::GM; ++g) mx = max(mx, red[g * W::BN + c]);
+    if (c0 + c < cmax) part[c0 + c] = mx;
+  }
+}
+
+// The sliced Gram's maxima slot of row tile tm (see q_fused_max).
+__device__ __forceinline__ uint32_t* colmax_slot(const Launch& L, const MatDesc& d, int tm) {
+  return reinterpret_cast<uint32_t*>(L.ws + d.oQ + q_max_off(max(d.m, d.n), d.r)) + tm * q_cols(d.r);
+}
+
 template <typename GT, bool VEC, bool FULL>
 __device__ __forceinline__ void mv3b_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
                                           int s, int tm, int tn, int kbeg, int kend, u32x4* smem) {
@@ -598,6 +634,8 @@ __device__ __forceinline__ void mv3b_body(const Launch& L, const MatDesc& d, con
                    ? reinterpret_cast<float*>(L.ws + d.oP)
                    : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.m * d.r;
   store_tile_w<WB>(out, d.r, tm * WB::BM, tn * WB::BN, d.m, d.r, acc);
+  if (q_fused_max(d.oQ, ci.splits, ci.tx))
+    store_colmax<WB>(colmax_slot(L, d, tm), tm * WB::BM, tn * WB::BN, d.m, d.r, acc, smem);
 }
 
 template <typename GT, bool VEC>
@@ -642,6 +680,8 @@ __device__ __forceinline__ void mtu3b_body(const Launch& L, const MatDesc& d, co
                    ? reinterpret_cast<float*>(L.ws + d.oW)
                    : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.n * d.r;
   store_tile_w<WB>(out, d.r, tm * WB::BM, tn * WB::BN, d.n, d.r, acc);
+  if (q_fused_max(d.oQ, ci.splits, ci.tx))
+    store_colmax<WB>(colmax_slot(L, d, tm), tm * WB::BM, tn * WB::BN, d.n, d.r, acc, smem);
 }
 
 template <typename GT, bool VEC>
