@@ -83,6 +83,8 @@ __device__ __forceinline__ void update_epilogue_full(const Launch& L, const MatD
     o2[j] = static_cast<uint32_t>(sizeof(GT)) * e;
   }
   const float eta = L.eta, beta = L.beta;
+  // X, G and R are streamed once: nontemporal accesses keep them from
+  // displacing the rank-r panels that the tiles still running read
 #pragma unroll
   for (int g0 = 0; g0 < NGRP; g0 += GPB) {
     float gv[E], rv[E], xv[E];
@@ -96,10 +98,10 @@ __device__ __forceinline__ void update_epilogue_full(const Launch& L, const MatD
       const gptr<const float> rp = uniform_ptr(to_global(static_cast<const float*>(d.R)) + e0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if constexpr (sizeof(GT) == 2) gv[4 * b + j] = bf16_to_f32(*byte_off(gp, o2[j]));
-        else gv[4 * b + j] = *byte_off(gp, o2[j]);
-        rv[4 * b + j] = *byte_off(rp, o4[j]);
-        xv[4 * b + j] = *byte_off(xp, o4[j]);
+        if constexpr (sizeof(GT) == 2) gv[4 * b + j] = bf16_to_f32(__builtin_nontemporal_load(byte_off(gp, o2[j])));
+        else gv[4 * b + j] = __builtin_nontemporal_load(byte_off(gp, o2[j]));
+        rv[4 * b + j] = __builtin_nontemporal_load(byte_off(rp, o4[j]));
+        xv[4 * b + j] = __builtin_nontemporal_load(byte_off(xp, o4[j]));
       }
     }
 #pragma unroll
@@ -111,8 +113,8 @@ __device__ __forceinline__ void update_epilogue_full(const Launch& L, const MatD
       const gptr<float> rp = uniform_ptr(to_global(d.R) + e0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        *byte_off(xp, o4[j]) = xv[4 * b + j] - eta * ax[fm][fn][4 * q + j];
-        *byte_off(rp, o4[j]) = beta * ((gv[4 * b + j] + rv[4 * b + j]) - ar[fm][fn][4 * q + j]);
+        __builtin_nontemporal_store(xv[4 * b + j] - eta * ax[fm][fn][4 * q + j], byte_off(xp, o4[j]));
+        __builtin_nontemporal_store(beta * ((gv[4 * b + j] + rv[4 * b + j]) - ar[fm][fn][4 * q + j]), byte_off(rp, o4[j]));
       }
     }
   }
