@@ -268,19 +268,28 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
 
 // One grouped launch per batch of at most kMaxClasses classes.  `fill`
 // sets the per-class work shape (returns false to leave a class out).
+// Classes with the longest reduction per work item go first (longest job
+// first), so that a launch does not end on a last round of its slowest
+// blocks; classes of equal length keep their order.
 template <class Fill, class Go>
 hipError_t grouped(const dion_plan& p, const Launch& base, Fill fill, Go go) {
-  Launch L = base;
-  L.nclass = 0;
-  L.total = 0;
+  std::vector<ClassInfo> todo;
   for (const ClassRec& c : p.cls) {
     ClassInfo ci{};
     if (!fill(c, ci) || ci.tiles <= 0) continue;
     ci.first = c.first;
     ci.count = c.count;
+    todo.push_back(ci);
+  }
+  std::stable_sort(todo.begin(), todo.end(),
+                   [](const ClassInfo& a, const ClassInfo& b) { return a.klen > b.klen; });
+  Launch L = base;
+  L.nclass = 0;
+  L.total = 0;
+  for (ClassInfo ci : todo) {
     ci.base = L.total;
     L.cls[L.nclass++] = ci;
-    L.total += c.count * ci.tiles;
+    L.total += ci.count * ci.tiles;
     if (L.nclass == kMaxClasses) {
       const hipError_t e = go(L);
       if (e != hipSuccess) return e;
@@ -312,9 +321,11 @@ hipError_t gram(const dion_plan& p, Launch base, int which, hipStream_t st) {
     // factor left them: then one slice per 256-row tile), digit planes,
     // int8 digit products.  A sharded plan's W is the caller's sum over
     // the shards, so its maxima are taken afresh.
+    // (the region exists in every sliced-Gram plan: oQ != 0)
+    constexpr int64_t kHasRegion = 1;
     auto fused = [&](const ClassRec& c) {
-      return which == 0 ? c.bn_mv == 256 && q_fused_max(1, c.s_mv, cdiv(c.m, 256))
-                        : c.bn_mtu == 256 && !p.sharded && q_fused_max(1, c.s_mtu, cdiv(c.n, 256));
+      return which == 0 ? c.bn_mv == 256 && q_fused_max(kHasRegion, c.s_mv, cdiv(c.m, 256))
+                        : c.bn_mtu == 256 && !p.sharded && q_fused_max(kHasRegion, c.s_mtu, cdiv(c.n, 256));
     };
     auto qsplit = [&](const ClassRec& c, ClassInfo& ci) {
       const int rows = which == 0 ? c.m : c.n;
@@ -551,6 +562,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
       ci.tx = cdiv(c.m, bn == 256 ? 256 : 128);
       ci.ty = cdiv(c.n, bn == 256 ? 128 : bn);
       ci.tiles = ci.tx * ci.ty;
+      ci.klen = c.r;   // the update reduces over r; only orders the classes
       return true;
     }, [&](const Launch& L) { return launch_epi(L, p.gdtype, bn, p.vec, p.math, st); }));
   }
