@@ -36,8 +36,10 @@ __device__ __forceinline__ gptr<T> to_global(T* p) {
 // chunks dealt to the XCDs in turn: at any time all XCDs work on nearby
 // chunks, so a launch whose tiles differ in cost (different matrix shapes)
 // stays balanced across XCDs.  Blocks of a last, partial round of chunks
-// keep their own number.  The map is a bijection on [0, nb).
-constexpr int kXcdChunk = 64;
+// keep their own number.  The map is a bijection on [0, nb).  (On the 3B
+// stack, chunks of 32 took up to 0.8 ms per step less than chunks of 64,
+// level with 16; 8 and 128 were slower.)
+constexpr int kXcdChunk = 32;
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
   const int round = 8 * kXcdChunk;
   if (b >= nb / round * round) return b;
@@ -61,9 +63,10 @@ __device__ __forceinline__ void locate(const Launch& L, int t, MatDesc& d,
 // Grouped tile order inside one matrix's tx x ty tile grid: consecutive
 // work items walk down GM tile rows of one tile column before moving to the
 // next column, so the tiles resident at the same time share both operand
-// panels in L2 (about GM row panels and a few column panels).
+// panels in L2 (about GM row panels and a few column panels).  (GM = 4 took
+// about 0.6 ms per step less than 8 on the 3B stack; 2 and 16 were slower.)
 __device__ __forceinline__ void tile_order(int local, int tx, int ty, int& tm, int& tn) {
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int per_group = GM * ty;
   const int g = local / per_group;
   const int first = g * GM;
