@@ -258,7 +258,9 @@ __global__ __launch_bounds__(kThreads) void k_chol_panel(Launch L) {
 //           j >= i, and Y_ic for c <= kb + 1.  Y_kb,(kb+1) lies above Y's
 //           diagonal and is never written, so column block kb + 1 takes the
 //           second panel only; Y_i,kb and Y_i,(kb+1) are first writes.
-__global__ __launch_bounds__(kThreads) void k_chol_trail(Launch L) {
+// Four blocks per CU (at most 128 registers per lane): more wavefronts to
+// cover the operand loads, which each wavefront issues all at once.
+__global__ __launch_bounds__(kThreads, 4) void k_chol_trail(Launch L) {
   MatDesc d;
   ClassInfo ci;
   int local;
