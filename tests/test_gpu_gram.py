@@ -93,3 +93,12 @@ def test_sliced_gram_column_scales(gpu_lib):
     say(f"gram {m}x{n} r={r} column scales 1e-30..1e30")
     s8, s64 = _compare(gpu_lib, c, "f32", v_scale=scale)
     assert np.all(s8[5, :] == 0.0) and np.all(s8[:, 5] == 0.0)
+
+
+@pytest.mark.parametrize("m", [16384, 16640])
+def test_sliced_gram_fused_maxima_boundary(gpu_lib, m):
+    # P = M V on the 256 x 256 split-bfloat16 tiles without a reduction
+    # split: at most 64 row tiles (16,384 rows) leave their column maxima
+    # for the Gram matrix; 65 row tiles fall back to the column-maximum pass
+    say(f"gram {m}x256 r=256 bf16x3 (row tiles {m // 256 + (m % 256 > 0)})")
+    _compare(gpu_lib, _case(m, 256, 256, seed=8), "bf16x3")
