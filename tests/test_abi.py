@@ -135,3 +135,26 @@ def test_gram_variant_bit(lib):
     assert f64 > 0
     assert sliced - f64 >= 5 * r * max(m, n)
     assert lib.dion_workspace_size(m, n, r, 1 | 0x800, 1) == 0
+
+
+def test_binding_constants_match_header():
+    # the binding's flag and status values are the header's #defines
+    here = os.path.dirname(os.path.abspath(__file__))
+    text = open(os.path.join(here, "..", "include", "dion.h")).read()
+    defs = {k: int(v, 0) for k, v in re.findall(r"#define\s+(DION_\w+)\s+\(?(-?(?:0x)?[0-9a-fA-F]+)\)?", text)}
+    assert defs["DION_VARIANT_DION"] == dion.VARIANTS["dion"]
+    assert defs["DION_VARIANT_ORTH"] == dion.VARIANTS["orth"]
+    assert defs["DION_MATH_F32"] == dion.MATH["f32"]
+    assert defs["DION_MATH_BF16X3"] == dion.MATH["bf16x3"]
+    assert defs["DION_GRAM_F64"] == dion.GRAM_F64
+    assert defs["DION_SHARDED"] == dion.SHARDED
+    assert defs["DION_SHARD_GRAM"] == dion.SHARD_GRAM and defs["DION_SHARD_W"] == dion.SHARD_W
+    assert defs["DION_OK"] == dion.OK and defs["DION_ERR_INVALID_ARG"] == dion.ERR_INVALID_ARG
+    assert defs["DION_ERR_WORKSPACE"] == dion.ERR_WORKSPACE and defs["DION_ERR_HIP"] == dion.ERR_HIP
+    assert defs["DION_ERR_BREAKDOWN"] == dion.ERR_BREAKDOWN
+    assert (defs["DION_STATUS_ORTH_P"], defs["DION_STATUS_ORTH_W"], defs["DION_STATUS_COLNORM"]) == \
+        (dion.STATUS_ORTH_P, dion.STATUS_ORTH_W, dion.STATUS_COLNORM)
+    # the three flag groups do not overlap
+    assert not (defs["DION_VARIANT_MASK"] & (defs["DION_MATH_MASK"] | defs["DION_SHARDED"] | defs["DION_GRAM_F64"]))
+    assert not (defs["DION_MATH_MASK"] & (defs["DION_SHARDED"] | defs["DION_GRAM_F64"]))
+    assert not (defs["DION_SHARDED"] & defs["DION_GRAM_F64"])
