@@ -17,10 +17,23 @@
  *   V   <- Vbar                        warm start of the next step
  *
  * orth(A) is the Q factor of the thin QR factorization A = Q T whose upper
- * triangular T has a positive diagonal; that choice makes Q unique for a
- * full-rank A.  The library computes it by CholeskyQR applied twice
- * (float32 Gram products on the matrix cores, float64 Cholesky and triangular
- * inverse).
+ * triangular T has a positive diagonal (the symbol list defines orth as the
+ * QR orthonormalization of the column space; the positive diagonal makes Q
+ * unique for a full-rank A).  The library computes it by CholeskyQR: a
+ * float64 Gram matrix (assembled from exact int8 digit products on the
+ * matrix cores by default, see DION_GRAM_F64), a blocked float64 Cholesky
+ * factorization S = T^T T that also yields T^{-T}, and the product
+ * A T^{-1} on the matrix cores.  The pivots tell how well-conditioned A is
+ * (pivot j over S_jj is about 1 / kappa^2 at worst):
+ *   - kappa below about 1e3 (every pivot ratio >= 1e-6): that one pass;
+ *   - up to about 1e4: a second pass on the result (CholeskyQR2) with a
+ *     float64 Gram matrix and float64 products;
+ *   - beyond that, or a failed pivot: the first pass is redone with a
+ *     diagonal shift on a float64 Gram matrix (shifted CholeskyQR), then
+ *     the second pass follows.
+ * The choice is made per matrix on the device.  A factor that is rank-
+ * deficient to float32 accuracy (the second pass finds a pivot ratio below
+ * 2 r 2^-48) is a breakdown (see below).
  *
  * Conventions for every entry point:
  *   - All functions are extern "C"; no C++ exception crosses the boundary.
@@ -35,16 +48,17 @@
  *     load path.
  *   - stream is a hipStream_t (NULL = the default stream).  Work is only
  *     enqueued: the calls return before the GPU finishes and never
- *     synchronize the host, except dion_status.  Buffers must stay valid
- *     until the enqueued work completes.
+ *     synchronize the host, except dion_status, dion_plan_destroy and
+ *     dion_plan_timing_enable / _read, which wait for work they must read
+ *     or free.  Buffers must stay valid until the enqueued work completes.
  *   - Argument errors are reported synchronously, before any HIP call is
  *     made, and leave every buffer untouched.
- *   - A numerical breakdown (orth of a numerically rank-deficient or
- *     non-finite factor; a zero or non-finite column norm for Dion) can only
- *     be seen on the device.  It is recorded in a status word inside the
- *     workspace, and every later kernel of that matrix skips its writes, so
- *     X, R and V of that matrix keep their previous contents bit for bit.
- *     Read it with dion_status.
+ *   - A numerical breakdown (orth of a factor that is rank-deficient to
+ *     float32 accuracy or not finite; a zero or non-finite column norm for
+ *     Dion) can only be seen on the device.  It is recorded in a status
+ *     word inside the workspace, and every later kernel of that matrix skips
+ *     its writes, so X, R and V of that matrix keep their previous contents
+ *     bit for bit.  Read it with dion_status.
  */
 #ifndef LIBDION_DION_H_
 #define LIBDION_DION_H_
@@ -112,7 +126,9 @@ extern "C" {
  *               (rp = r rounded up to 64); stage 1 reads only the upper
  *               triangle of its leading r x r block
  *   stage 1: T from the summed Gram matrix, U_i = P_i T^{-1},
- *            W_i = M_i^T U_i
+ *            W_i = M_i^T U_i (one CholeskyQR pass: a further pass would
+ *            need another exchange, so a pivot ratio below 1e-6 is a
+ *            breakdown here; orth(W) in stage 2 takes every pass it needs)
  *            -> exchange DION_SHARD_W: float32, n x r row-major
  *   stage 2: Vbar from the summed W (computed identically on every shard),
  *            X_i and R_i updated, Vbar written into the shard's V.
@@ -185,10 +201,14 @@ int dion_step(float* X, const void* G, float* R, float* V,
 
 /* Grouped step: the same update applied to each matrix of a list (for
  * example all weight matrices of a model) with a handful of kernel launches
- * for the whole list.  Matrices may have different shapes.  Equivalent to a
- * dion_step call per matrix.  The matrix list is copied; the call keeps an
- * internal cache of plans keyed by the list, so repeating the same list
- * costs no host-side setup. */
+ * for the whole list.  The pages apply the step to every weight matrix
+ * independently (Orth-Dion page, equation block, per matrix X); the nearest
+ * thing they describe to running many of them together is the Dion3
+ * abstract's megabatching.  Matrices may have different shapes.  Equivalent
+ * to a dion_step call per matrix.  The matrix list is copied; the call
+ * keeps an internal cache of plans keyed by the list, so repeating the same
+ * list costs no host-side setup (a plan evicted from the cache is freed
+ * once its last copy has completed, without waiting for it). */
 size_t dion_workspace_size_batched(const dion_matrix* mats, int count,
                                    int variant, int g_dtype);
 int dion_step_batched(const dion_matrix* mats, int count, float eta, float beta,
@@ -214,6 +234,22 @@ int dion_plan_shard_stage(dion_plan* plan, int stage, float eta, float beta,
 int dion_plan_shard_buffer(const dion_plan* plan, int which, int index,
                            size_t* offset, size_t* bytes);
 
+/* Inspection of a plan's intermediate factors.  After a step of `plan` has
+ * completed on the stream, the workspace holds, for matrix `index` (its
+ * position in the plan's list) unless it broke down:
+ *   DION_BUF_P  P = M V                 float32, m x r row-major
+ *   DION_BUF_U  U = orth(P)             float32, m x r row-major
+ *   DION_BUF_W  W = M^T U               float32, n x r row-major
+ * dion_plan_buffer gives the byte offset from the workspace base and the
+ * size of one of them.  They stay valid until the next step on that
+ * workspace.  Errors: DION_ERR_INVALID_ARG for a null plan or output
+ * pointer, `which` outside DION_BUF_* or `index` outside the list. */
+#define DION_BUF_W    1   /* the same value as DION_SHARD_W */
+#define DION_BUF_P    2
+#define DION_BUF_U    3
+int dion_plan_buffer(const dion_plan* plan, int which, int index,
+                     size_t* offset, size_t* bytes);
+
 /* Phase timing, for measurement.  A step runs five phases, in order:
  *   0  P = M V            1  U = orth(P)          2  W = M^T U
  *   3  Vbar (orth(W) or column normalization; with split-bfloat16 products
@@ -235,7 +271,10 @@ int dion_plan_timing_read(dion_plan* plan, double* ms_per_phase, int* steps);
  * length for a grouped step).  per_matrix (optional, count ints) receives
  * each matrix's DION_STATUS_* flags, in the caller's list order.
  * Returns DION_OK, DION_ERR_BREAKDOWN if any matrix broke down, or an
- * argument / HIP error. */
+ * argument / HIP error.  The workspace does not record how many matrices
+ * the last step had, so the caller passes `count`; a grouped step can
+ * break down in some matrices only, so the flags come per matrix rather
+ * than as one code. */
 int dion_status(const void* workspace, int count, void* stream, int* per_matrix);
 
 #ifdef __cplusplus

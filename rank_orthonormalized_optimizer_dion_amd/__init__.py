@@ -33,6 +33,7 @@ MATH = {"f32": 0x000, "bf16x3": 0x100}
 SHARDED = 0x200
 GRAM_F64 = 0x400   # OR into math: float64 MFMA Gram matrix instead of sliced int8
 SHARD_GRAM, SHARD_W = 0, 1
+BUF_W, BUF_P, BUF_U = 1, 2, 3   # dion_plan_buffer: intermediate factors of the last step
 STATUS_ORTH_P, STATUS_ORTH_W, STATUS_COLNORM = 1, 2, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +98,8 @@ def load() -> ctypes.CDLL:
         "dion_plan_shard_stage": (c_int, [vp, c_int, c_f, c_f, vp, c_size, vp]),
         "dion_plan_shard_buffer": (c_int, [vp, c_int, c_int, ctypes.POINTER(c_size),
                                            ctypes.POINTER(c_size)]),
+        "dion_plan_buffer": (c_int, [vp, c_int, c_int, ctypes.POINTER(c_size),
+                                     ctypes.POINTER(c_size)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -309,6 +312,22 @@ class Plan:
             return raw.view(torch.float64).view(rp, rp)
         n, r = self._mats[index][3].shape
         return raw.view(torch.float32).view(n, r)
+
+    def buffer(self, workspace, which: int, index: int):
+        """Intermediate factor `which` (BUF_P: P = M V, BUF_U: U = orth(P),
+        both m x r; BUF_W: W = M^T U, n x r; float32) of matrix `index` after
+        the last step on `workspace`, as a view into it
+        (dion_plan_buffer)."""
+        torch = _torch()
+        off, nbytes = ctypes.c_size_t(), ctypes.c_size_t()
+        rc = self._lib.dion_plan_buffer(self._h, int(which), int(index), ctypes.byref(off),
+                                        ctypes.byref(nbytes))
+        if rc != OK:
+            raise _err(rc)
+        raw = workspace.view(torch.uint8)[off.value:off.value + nbytes.value]
+        X, V = self._mats[index][0], self._mats[index][3]
+        rows = V.shape[0] if which == BUF_W else X.shape[0]
+        return raw.view(torch.float32).view(rows, V.shape[1])
 
     PHASES = ("mv", "orth_p", "mtu", "right", "update")
 

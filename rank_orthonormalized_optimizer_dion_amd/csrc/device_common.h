@@ -60,6 +60,70 @@ __device__ __forceinline__ void locate(const Launch& L, int t, MatDesc& d,
   d = L.table ? L.table[ci.first + mi] : L.inl;
 }
 
+// Whether a kernel leaves matrix d alone: it broke down earlier in the
+// step, or the launch's gate excludes it (status word and gates: see
+// dion_types.h).
+__device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
+  const int32_t s = L.status[d.slot];
+  if (s & kStatusMask) return true;
+  switch (L.gate) {
+    case kGateFirst: return (s & kCtlRetry) != 0;
+    case kGateOne: return (s & kCtlTwo) != 0;
+    case kGateRetry: return (s & kCtlRetry) == 0;
+    case kGateTwo: return (s & kCtlTwo) == 0;
+    default: return false;
+  }
+}
+
+// The factors of orth(): pass 1 reads Q0 = P (which = 0) or W (which = 1);
+// the result is U (workspace oB) or Vbar (written into V).  When a second
+// pass follows (kCtlTwo), the first writes oC and the second reads it.
+__device__ __forceinline__ const float* orth_src(const Launch& L, const MatDesc& d) {
+  if (L.pass == 2) return reinterpret_cast<const float*>(L.ws + d.oC);
+  return reinterpret_cast<const float*>(L.ws + (L.which == 0 ? d.oP : d.oW));
+}
+__device__ __forceinline__ float* orth_dst(const Launch& L, const MatDesc& d) {
+  if (L.pass == 1 && (L.status[d.slot] & kCtlTwo)) return reinterpret_cast<float*>(L.ws + d.oC);
+  return L.which == 0 ? reinterpret_cast<float*>(L.ws + d.oB) : d.V;
+}
+
+// Whether orth() of matrix d needs more than its first CholeskyQR pass,
+// decided once the first pass's Cholesky factorization is complete: 0 (one
+// pass), kCtlTwo (a second pass) or kCtlTwo | kCtlRetry (the first pass
+// again with a shift, then the second).  One pass leaves Q T^{-1} with an
+// orthogonality error of about lambda_min(C)^-1 times the Gram matrix's
+// relative error (C the column-scaled Gram matrix); t = trace(C^{-1}) lies
+// between 1 / lambda_min(C) and r / lambda_min(C), so t <= kTraceTwo r keeps
+// that error at float32's level (the workloads here stay below 2 r), and
+// t > kTraceRetry r means the first pass's result is too far from
+// orthonormal for a second pass to repair.  The chain's kernels leave t in
+// per-block partial sums (see k_chol.hip) and the diagonal steps may
+// already have asked for more (small pivot ratios, control bits); every
+// workgroup that asks sums the partials in the same order, so all of them
+// reach the same answer.  Plans without retries (row-sharded P) always
+// take one pass.
+constexpr double kTraceTwo = 1e3;
+constexpr double kTraceRetry = 1e7;
+__device__ __forceinline__ int32_t orth_decision(const Launch& L, const MatDesc& d) {
+  if (!L.retry) return 0;
+  const int32_t s = L.status[d.slot];
+  if (s & kCtlRetry) return kCtlTwo | kCtlRetry;
+  const int nblk = d.rp / kCholNB;
+  const double* part = reinterpret_cast<const double*>(L.ws + d.oD) + kCholNB * kCholNB + d.rp;
+  double t = 0.0;
+  for (int jb = 0; jb < nblk; ++jb)
+    for (int c = 0; c <= jb; ++c) t += part[jb * nblk + c];
+  if (!(t <= kTraceRetry * d.r)) return kCtlTwo | kCtlRetry;
+  if (!(t <= kTraceTwo * d.r) || (s & kCtlTwo)) return kCtlTwo;
+  return 0;
+}
+
+// Workgroups of a launch whose kernel loops over its work items: launches
+// that only some matrices need (gates kGateRetry and kGateTwo) run at most
+// this many, so that they cost little when no matrix needs them.
+constexpr int kGatedGrid = 1024;
+inline __host__ __device__ int gated_grid(int total) { return total < kGatedGrid ? total : kGatedGrid; }
+
 // Grouped tile order inside one matrix's tx x ty tile grid: consecutive
 // work items walk down GM tile rows of one tile column before moving to the
 // next column, so the tiles resident at the same time share both operand

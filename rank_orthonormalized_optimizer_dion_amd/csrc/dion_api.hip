@@ -4,7 +4,11 @@
 // One step (Orth-Dion page, equation block; Dion's rule from its closing
 // remark) is enqueued as:
 //   k_mv [+k_reduce]                 P = (G + R) V
-//   CholeskyQR on P -> U             k_gram (float64), k_chol_*, k_trmm
+//   CholeskyQR on P -> U             Gram (k_qmax, k_qslice, k_gram8 or
+//                                    k_gram), k_chol_*, k_trmm; for
+//                                    ill-conditioned P a shifted retry and a
+//                                    second pass (k_gram, k_chol_one,
+//                                    k_trmm64), gated on the device
 //   k_mtu [+k_reduce]                W = (G + R)^T U
 //   Orth-Dion: CholeskyQR on W -> V      Dion: k_colnorm, k_colscale -> V
 //   k_epi                            X -= eta U V^T, R = beta (G + R - U W^T)
@@ -249,11 +253,16 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     };
     d.oP = take(m * r * 4);
     d.oB = take(m * r * 4);
+    // first-pass output of a two-pass orth: of P (m rows), and of W (n
+    // rows) for Orth-Dion
+    d.oC = take((p.variant == DION_VARIANT_ORTH ? std::max(m, n) : m) * r * 4);
     d.oW = take(n * r * 4);
     d.oS = take(static_cast<size_t>(std::max(k.s_gp, k.s_gw)) * rp * rp * 8);
     d.oA = take(rp * rp * 8);
     d.oY = take(rp * rp * 8);
-    d.oD = take((kCholNB * kCholNB + rp) * 8);
+    // diagonal-block inverse, diag(S), then the trace partials of the
+    // first pass (one per 64 x 64 block of T^{-T})
+    d.oD = take((kCholNB * kCholNB + rp + (rp / kCholNB) * (rp / kCholNB)) * 8);
     d.oN = take(r * 4);
     const size_t kpart = std::max(k.s_mv > 1 ? k.s_mv * m * r : 0, k.s_mtu > 1 ? k.s_mtu * n * r : 0);
     d.oK = kpart ? take(kpart * 4) : 0;
@@ -315,6 +324,7 @@ hipError_t grouped(const dion_plan& p, const Launch& base, Fill fill, Go go) {
 hipError_t gram(const dion_plan& p, Launch base, int which, hipStream_t st) {
   base.which = which;
   base.pass = 1;
+  base.gate = kGateAll;
   base.flag = which == 0 ? DION_STATUS_ORTH_P : DION_STATUS_ORTH_W;
   if (p.gram8) {
     // column maxima over row slices (unless the kernel that wrote the
@@ -373,10 +383,47 @@ hipError_t gram(const dion_plan& p, Launch base, int which, hipStream_t st) {
   return hipSuccess;
 }
 
+// The parts of orth() that only ill-conditioned factors take (gated on the
+// device, see dion_types.h): the shifted first pass (float64 Gram matrix and
+// the whole factorization of each matrix in one workgroup), and the float64
+// triangular multiply of the first pass followed by the second pass.  Every
+// launch runs a capped grid, so it costs little when no matrix needs it.
+hipError_t rare_gram(const dion_plan& p, const Launch& base, int which, hipStream_t st) {
+  return grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+    const int nt = cdiv(c.r, 64);
+    ci.tx = nt;
+    ci.splits = which == 0 ? c.s_gp : c.s_gw;
+    ci.klen = which == 0 ? c.kl_gp : c.kl_gw;
+    ci.tiles = nt * (nt + 1) / 2 * ci.splits;
+    return true;
+  }, [&](const Launch& L) { return launch_gram(L, 64, p.vec, st); });
+}
+
+hipError_t rare_chol(const dion_plan& p, const Launch& base, int which, hipStream_t st) {
+  return grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+    ci.splits = which == 0 ? c.s_gp : c.s_gw;
+    ci.tiles = 1;
+    return true;
+  }, [&](const Launch& L) { return launch_chol_one(L, st); });
+}
+
+hipError_t rare_trmm(const dion_plan& p, const Launch& base, int which, hipStream_t st) {
+  return grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+    ci.tx = cdiv(which == 0 ? c.m : c.n, 64);
+    ci.ty = cdiv(c.r, 64);
+    ci.tiles = ci.tx * ci.ty;
+    return true;
+  }, [&](const Launch& L) { return launch_trmm64(L, st); });
+}
+
 hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
   base.which = which;
   base.pass = 1;
   base.flag = which == 0 ? DION_STATUS_ORTH_P : DION_STATUS_ORTH_W;
+  // More passes need the whole factor here; the row-sharded P is a sum the
+  // caller forms between stages, so its single pass is final.
+  base.retry = p.sharded && which == 0 ? 0 : 1;
+  base.gate = kGateAll;   // k_chol_init clears the control bits
   int max_nblk = 0;
   for (const ClassRec& c : p.cls) max_nblk = std::max(max_nblk, c.rp / kCholNB);
   DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
@@ -400,6 +447,7 @@ hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
       return true;
     }, [&](const Launch& L) { return launch_chol_panel(L, st); });
   };
+  base.gate = kGateFirst;
   for (int kb = 0; kb < max_nblk; kb += 2) {
     DION_TRY(diag_panel(kb));
     if (kb + 1 >= max_nblk) break;
@@ -419,6 +467,9 @@ hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
       return true;
     }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
   }
+  // the float32 triangular multiply of single-pass matrices; its
+  // workgroups also decide, per matrix, whether a second pass is needed
+  base.gate = kGateOne;
   for (int bn : {128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_r != bn) return false;
@@ -427,6 +478,19 @@ hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
       ci.tiles = ci.tx * ci.ty;
       return true;
     }, [&](const Launch& L) { return launch_trmm(L, bn, p.vec, p.math, st); }));
+  }
+  if (base.retry) {
+    Launch rl = base;   // ill-conditioned: the first pass again, shifted
+    rl.gate = kGateRetry;
+    DION_TRY(rare_gram(p, rl, which, st));
+    DION_TRY(rare_chol(p, rl, which, st));
+    Launch tl = base;   // the first pass's product in float64, then the second pass
+    tl.gate = kGateTwo;
+    DION_TRY(rare_trmm(p, tl, which, st));
+    tl.pass = 2;
+    DION_TRY(rare_gram(p, tl, which, st));
+    DION_TRY(rare_chol(p, tl, which, st));
+    DION_TRY(rare_trmm(p, tl, which, st));
   }
   return hipSuccess;
 }
@@ -633,9 +697,35 @@ int plan_step(dion_plan* p, float eta, float beta, void* ws, size_t bytes, hipSt
 }
 
 // Cache of grouped plans keyed by the matrix list (most recent first).
+// An evicted plan whose last table copy may still be in flight waits in
+// g_retired until its event has completed (polled, never waited for), so
+// that dion_step_batched does not block the host.
 constexpr size_t kCacheSize = 8;
 std::mutex g_cache_mu;
 std::list<dion_plan*> g_cache;
+std::list<dion_plan*> g_retired;
+
+void retire(dion_plan* p) {
+  if (p->ev_pending && hipEventQuery(p->ev) != hipSuccess) {
+    g_retired.push_back(p);
+    return;
+  }
+  p->ev_pending = false;
+  plan_free(p);
+}
+
+void sweep_retired() {
+  for (auto it = g_retired.begin(); it != g_retired.end();) {
+    dion_plan* p = *it;
+    if (hipEventQuery(p->ev) == hipSuccess) {
+      p->ev_pending = false;
+      plan_free(p);
+      it = g_retired.erase(it);
+    } else {
+      ++it;
+    }
+  }
+}
 
 std::vector<uint64_t> make_key(const dion_matrix* mats, int count, int variant, int gdtype) {
   std::vector<uint64_t> k;
@@ -660,7 +750,7 @@ std::vector<uint64_t> make_key(const dion_matrix* mats, int count, int variant, 
 
 using namespace dion;
 
-DION_API int dion_version(void) { return 100; }
+DION_API int dion_version(void) { return 200; }
 
 DION_API const char* dion_error_string(int code) {
   switch (code) {
@@ -767,6 +857,21 @@ DION_API int dion_plan_shard_buffer(const dion_plan* plan, int which, int index,
   return DION_ERR_INVALID_ARG;
 }
 
+DION_API int dion_plan_buffer(const dion_plan* plan, int which, int index, size_t* offset,
+                              size_t* bytes) {
+  if (!plan || !offset || !bytes) return DION_ERR_INVALID_ARG;
+  if (which != DION_BUF_P && which != DION_BUF_U && which != DION_BUF_W) return DION_ERR_INVALID_ARG;
+  if (index < 0 || index >= plan->count) return DION_ERR_INVALID_ARG;
+  for (const MatDesc& d : plan->table) {
+    if (d.slot != index) continue;
+    const int64_t off = which == DION_BUF_P ? d.oP : which == DION_BUF_U ? d.oB : d.oW;
+    *offset = static_cast<size_t>(off);
+    *bytes = static_cast<size_t>(which == DION_BUF_W ? d.n : d.m) * d.r * 4;
+    return DION_OK;
+  }
+  return DION_ERR_INVALID_ARG;
+}
+
 DION_API int dion_plan_timing_enable(dion_plan* plan, int max_steps) {
   if (!plan || max_steps < 0 || max_steps > (1 << 20)) return DION_ERR_INVALID_ARG;
   if (!plan->tev.empty()) {
@@ -817,6 +922,7 @@ DION_API int dion_step_batched(const dion_matrix* mats, int count, float eta, fl
   if (!mats || count < 1 || (variant & DION_SHARDED)) return DION_ERR_INVALID_ARG;
   std::vector<uint64_t> key = make_key(mats, count, variant, g_dtype);
   std::lock_guard<std::mutex> lock(g_cache_mu);
+  sweep_retired();
   dion_plan* hit = nullptr;
   for (auto it = g_cache.begin(); it != g_cache.end(); ++it)
     if ((*it)->key == key) {
@@ -831,7 +937,7 @@ DION_API int dion_step_batched(const dion_matrix* mats, int count, float eta, fl
     p->key = std::move(key);
     hit = p;
     if (g_cache.size() >= kCacheSize) {
-      plan_free(g_cache.back());
+      retire(g_cache.back());
       g_cache.pop_back();
     }
   }
@@ -849,8 +955,9 @@ DION_API int dion_status(const void* workspace, int count, void* stream, int* pe
   if (hipStreamSynchronize(s) != hipSuccess) return DION_ERR_HIP;
   int rc = DION_OK;
   for (int i = 0; i < count; ++i) {
-    if (per_matrix) per_matrix[i] = st[i];
-    if (st[i] != 0) rc = DION_ERR_BREAKDOWN;
+    const int flags = st[i] & kStatusMask;   // the breakdown flags, not the control bits
+    if (per_matrix) per_matrix[i] = flags;
+    if (flags != 0) rc = DION_ERR_BREAKDOWN;
   }
   return rc;
 }

@@ -55,8 +55,10 @@ struct MatDesc {
   int32_t m, n, r, rp;
   int32_t slot;      // index in the caller's list = status word index
   int32_t pad0;
-  int64_t oP;        // m x r      float32: P = M V, then U
-  int64_t oB;        // max(m,n) x r float32: first CholeskyQR pass output
+  int64_t oP;        // m x r      float32: P = M V
+  int64_t oB;        // m x r      float32: U = orth(P)
+  int64_t oC;        // max(m,n) x r float32: the first pass's output when
+                     // orth takes a second CholeskyQR pass
   int64_t oW;        // n x r      float32: W = M^T U
   int64_t oS;        // splits x rp x rp float32: Gram partial sums
   int64_t oA;        // rp x rp    float64: Cholesky work matrix (upper blocks)
@@ -76,6 +78,33 @@ struct MatDesc {
                      // exponents of the factor being orthogonalized
                      // (layout above, rows_max = max(m, n)); 0 if unused
 };
+
+// Status word of a matrix (one int32 per matrix slot).  Bits 0-7 are the
+// breakdown flags dion_status reports (DION_STATUS_*); any of them makes
+// every later kernel of the step skip the matrix.  Bits 8-9 steer the
+// factorization in progress (orth of P, then of W) and are cleared at its
+// start:
+//   kCtlTwo    the first CholeskyQR pass found a pivot ratio below
+//              kRatioTwo: its triangular multiply runs in float64 into oC,
+//              and a second pass (float64 Gram, float64 triangular
+//              multiply) writes the result
+//   kCtlRetry  the first pass found a pivot ratio below kRatioRetry or a
+//              failed pivot: its factorization is abandoned and a shifted
+//              one on a float64 Gram replaces it (kCtlTwo is set as well)
+constexpr int32_t kStatusMask = 0xff;
+constexpr int32_t kCtlTwo = 1 << 8;
+constexpr int32_t kCtlRetry = 1 << 9;
+
+// Which matrices a kernel of an orth() factorization works on (Launch.gate):
+//   kGateAll    every matrix that has not broken down
+//   kGateFirst  the first pass's Cholesky steps: not the matrices whose
+//               factorization was abandoned (kCtlRetry)
+//   kGateOne    the first pass's float32 triangular multiply: only the
+//               matrices that take a single pass (no kCtlTwo)
+//   kGateRetry  the shifted factorization: only kCtlRetry
+//   kGateTwo    the float64 triangular multiply of the first pass and the
+//               whole second pass: only kCtlTwo
+enum Gate : int32_t { kGateAll = 0, kGateFirst = 1, kGateOne = 2, kGateRetry = 3, kGateTwo = 4 };
 
 // Matrices with the same (m, n, r) form a class; inside one launch every
 // matrix of a class owns `tiles` consecutive work items starting at `base`.
@@ -101,9 +130,12 @@ struct Launch {
   float eta, beta;
   int32_t kb;             // Cholesky block step
   int32_t which;          // 0: factor P (m rows), 1: factor W (n rows)
-  int32_t pass;           // CholeskyQR pass 1 or 2
+  int32_t pass;           // CholeskyQR pass 1 or 2 (the factor it reads and writes)
   int32_t flag;           // status bit of this factorization
   int32_t mode;           // Cholesky trailing update: 1 look-ahead block row, 2 the rest
+  int32_t gate;           // Gate: which matrices the launch works on
+  int32_t retry;          // first pass: 1 = small pivots lead to a second pass or
+                          // the shifted retry, 0 = they are breakdowns
 };
 
 }  // namespace dion

@@ -16,6 +16,13 @@
 //                 pass over the trailing matrix per two block steps
 // k_chol_init sums the Gram partials into A (float64) first and pads the
 // rows past r with the identity.
+//
+// The chain above is the first CholeskyQR pass of every factor.  A factor
+// whose pivots show it ill-conditioned takes more (the per-matrix status
+// bits of dion_types.h steer this on the device, so the host never waits):
+//   k_chol_one  the whole factorization of one matrix in one workgroup:
+//               the shifted retry of the first pass, and the second pass
+//   k_trmm64    Q T^{-1} with float64 products, rounded once to float32
 #include <math.h>
 
 #include "device_common.h"
@@ -27,16 +34,43 @@ namespace {
 
 constexpr int NB = kCholNB;
 
-// A pivot below this fraction of the column's original squared norm means
-// the factor's condition number is beyond about 1e3, where the float32
-// product Q T^{-1} would no longer have orthonormal columns to float32
-// accuracy: the factor is declared numerically rank-deficient.
-constexpr double kPivotTol = 1e-6;
+// Pivot ratio d_j / S_jj: the j-th pivot over column j's squared norm, the
+// squared sine of the angle between column j and the span of the columns
+// before it.  A pivot ratio below kRatioRetry (or a failed pivot) abandons
+// the first pass for the shifted retry; below kRatioTwo it asks for a
+// second pass.  The finer decision comes from the trace of C^{-1} (C the
+// column-scaled Gram matrix), which the chain gathers in per-block partial
+// sums (orth_decision in device_common.h).  Plans whose first pass cannot
+// be repeated (the row-sharded P, whose Gram matrix is summed by the
+// caller) treat a ratio below kRatioTwo as a breakdown.
+constexpr double kRatioTwo = 1e-6;
+constexpr double kRatioRetry = 1e-8;
 
-__device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
-  return L.status[d.slot] != 0;
+// Shift of the retry, relative to each column's squared norm: A = S +
+// s diag(S).  The float64 Gram matrix of a float32 factor of `rows` rows is
+// exact in its products and rounds its sums, so each entry is within
+// rows 2^-53 sqrt(S_ii S_jj), and the column-scaled error matrix within
+// r rows 2^-53 in norm; with the Cholesky's own rounding, (r rows + r^2)
+// 2^-50 is eight times what makes the shifted factorization succeed for any
+// factor with finite, nonzero columns.  It is kept at 2^-30 or more so that
+// T^{-1} (norm up to 1 / sqrt(s) in column-scaled units) stays small enough
+// for the float64 triangular multiply to leave an exactly dependent column
+// dependent to about 2^-53 sqrt(r) / s (see second_tol).  Every pivot ratio
+// is then at least about s, and Q1 = Q T^{-1} has a condition number of
+// about sqrt(s) kappa.
+__device__ __forceinline__ double retry_shift(int rows, int r) {
+  const double s = (static_cast<double>(r) * rows + static_cast<double>(r) * r) * 0x1p-50;
+  return s > 0x1p-30 ? s : 0x1p-30;
 }
 
+// Smallest pivot ratio the second pass accepts: r 2^-40.  A direction in
+// which Q is exactly deficient keeps, in Q1 = fl32(Q T^{-1}), a relative
+// size of at most about 2^-24 sqrt(r) from the float32 rounding and
+// 2^-53 sqrt(r) / s <= 2^-23 sqrt(r) from the float64 products: a pivot
+// ratio of order r 2^-46, which r 2^-40 clears by 2^6.  Genuinely
+// ill-conditioned factors give ratios near 1 / (s kappa^2), so factors up
+// to kappa of about 1e8 (beyond what float32 resolves) pass.
+__device__ __forceinline__ double second_tol(int r) { return r * 0x1p-40; }
 __device__ __forceinline__ double* dptr(const Launch& L, int64_t off) {
   return reinterpret_cast<double*>(L.ws + off);
 }
@@ -96,6 +130,9 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
   int local;
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
+  // A factorization starts with no control bits (no other kernel of this
+  // launch reads them)
+  if (local == 0 && threadIdx.x == 0) L.status[d.slot] &= kStatusMask;
   const int nblk = d.rp / NB;
   int p = local, bi = 0;
   while (p >= nblk - bi) {
@@ -152,17 +189,30 @@ __device__ __forceinline__ double rsqrt_nr(double x) {
   return y;
 }
 
-__global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
+// Sum of one value per thread over the workgroup, in a fixed order (lanes
+// by a butterfly, then the four wavefronts in turn), the same in every
+// thread.
+__device__ __forceinline__ double block_sum(double v) {
+  __shared__ double red[kThreads / 64];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// Factors diagonal block kb of matrix d (Dinv and Y_kk written to the
+// workspace).  A pivot fails when it is not above tol times the column's
+// original squared norm (or is not finite); returns false then, with
+// nothing written.  small: some pivot ratio was below kRatioTwo.
+__device__ __forceinline__ bool diag_block(const Launch& L, const MatDesc& d, int kb, double tol,
+                                           bool& small, double* part) {
   __shared__ double rowA[2][NB];
   __shared__ double rowZ[2][NB];
   __shared__ double sd[NB];
   __shared__ int badf[2];
-  MatDesc d;
-  ClassInfo ci;
-  int local;
-  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
-  if (skipped(L, d)) return;
-  const int kb = L.kb;
+  __shared__ int smallf;
   const int64_t rp = d.rp, o = static_cast<int64_t>(kb) * NB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   gptr<const double> A = to_global(dptr(L, d.oA) + o * rp + o);
@@ -173,6 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
     z[q] = 4 * q + wave == lane ? 1.0 : 0.0;
   }
   if (threadIdx.x < NB) sd[threadIdx.x] = dptr(L, d.oD)[NB * NB + o + threadIdx.x];
+  if (threadIdx.x == 0) smallf = 0;
   __syncthreads();
   bool bad = false;
 #pragma unroll
@@ -182,13 +233,16 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
       const int k = 4 * q + w, buf = k & 1;
       if (wave == w) {   // this wavefront holds row k
         const double dk = read_lane(a[q], k);
-        const bool ok = dk > kPivotTol * sd[k] && dk < INFINITY;
+        const bool ok = dk > tol * sd[k] && dk < INFINITY;
         const double inv = rsqrt_nr(dk), t = dk * inv;
         a[q] = lane > k ? a[q] * inv : (lane == k ? t : 0.0);
         z[q] = lane <= k ? z[q] * inv : 0.0;
         rowA[buf][lane] = a[q];
         rowZ[buf][lane] = z[q];
-        if (lane == 0) badf[buf] = ok ? 0 : 1;
+        if (lane == 0) {
+          badf[buf] = ok ? 0 : 1;
+          if (!(dk >= kRatioTwo * sd[k])) smallf = 1;
+        }
       }
       __syncthreads();
       // every read of the broadcast row is issued before the first use
@@ -210,18 +264,50 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
     }
     if (bad) break;
   }
-  if (bad) {
-    if (threadIdx.x == 0) atomicOr(&L.status[d.slot], L.flag);
-    return;
-  }
+  small = smallf != 0;
+  if (bad) return false;
   // Dinv = T_kk^{-1} = Z^T (upper triangular), Y_kk = Z (lower, zeros above).
   gptr<double> Dinv = to_global(dptr(L, d.oD));
   gptr<double> Y = to_global(dptr(L, d.oY) + o * rp + o);
+  double acc = 0.0;
 #pragma unroll
   for (int q = 0; q < NB / 4; ++q) {
     const int i = 4 * q + wave;
     Dinv[lane * NB + i] = lane <= i ? z[q] : 0.0;
     Y[i * rp + lane] = z[q];
+    acc += z[q] * z[q];
+  }
+  if (part) {
+    // this block's share of trace(C^{-1}): S_cc Y_jc^2 over its columns c < r
+    const double w = o + lane < d.r ? sd[lane] : 0.0;
+    const double t = block_sum(w * acc);
+    if (threadIdx.x == 0) *part = t;
+  }
+  return true;
+}
+
+// Diagonal block step of the first pass (one workgroup per matrix).
+// Partial sums of the trace of C^{-1} (C the column-scaled Gram matrix):
+// trace = sum over c <= j of S_cc Y_jc^2 (Y = T^{-T}, c < r), kept per
+// 64 x 64 block of Y in the workspace after diag(S), block (jb, c) at
+// jb * nblk + c.  Each is written once, by the kernel that leaves that
+// block of Y final.
+__device__ __forceinline__ double* trace_part(const Launch& L, const MatDesc& d, int jb, int c) {
+  return dptr(L, d.oD) + NB * NB + d.rp + static_cast<int64_t>(jb) * (d.rp / NB) + c;
+}
+
+__global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  bool small;
+  const bool ok = diag_block(L, d, L.kb, L.retry ? kRatioRetry : kRatioTwo, small,
+                             trace_part(L, d, L.kb, L.kb));
+  if (threadIdx.x == 0) {
+    if (!ok) atomicOr(&L.status[d.slot], L.retry ? (kCtlRetry | kCtlTwo) : L.flag);
+    else if (small && L.retry) atomicOr(&L.status[d.slot], kCtlTwo);
   }
 }
 
@@ -247,6 +333,25 @@ __global__ __launch_bounds__(kThreads) void k_chol_panel(Launch L) {
     for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
       for (int v = 0; v < 4; ++v) out[block_off(fm, fn, v, rp)] = acc[fm][fn][v];
+  if (local >= right) {
+    // block (kb, c) of Y is final: its share of trace(C^{-1})
+    const int c = local - right;
+    const double* sd = dptr(L, d.oD) + NB * NB + c * NB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double t = 0.0;
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+      const int col = (wave & 1) * 32 + fn * 16 + (lane & 15);
+      double q = 0.0;
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) q += acc[fm][fn][v] * acc[fm][fn][v];
+      t += c * NB + col < d.r ? sd[col] * q : 0.0;
+    }
+    t = block_sum(t);
+    if (threadIdx.x == 0) *trace_part(L, d, kb, c) = t;
+  }
 }
 
 // Trailing update of the factorization and of the identity block columns,
@@ -330,10 +435,181 @@ __global__ __launch_bounds__(kThreads, 4) void k_chol_trail(Launch L) {
       }
 }
 
+// The whole factorization of one matrix in one workgroup (the shifted
+// retry of the first pass, gate kGateRetry, and the second pass, gate
+// kGateTwo with pass 2): A from the Gram partials (plus s diag(S) for the
+// retry), then every block step in turn: the diagonal block, the panel
+// row, and the trailing update of A and of Y, with the same arithmetic as
+// the chain's kernels.  A failed pivot is a breakdown.  Work items: one per matrix,
+// taken in a loop so that a launch with few workgroups covers any list.
+__global__ __launch_bounds__(kThreads) void k_chol_one(Launch L) {
+  for (int t = blockIdx.x; t < L.total; t += gridDim.x) {
+    MatDesc d;
+    ClassInfo ci;
+    int local;
+    locate(L, t, d, ci, local);
+    if (skipped(L, d)) continue;
+    const int rows = L.which == 0 ? d.m : d.n;
+    const int nblk = d.rp / NB;
+    const int64_t rp = d.rp, plane = rp * rp;
+    const bool shifted = L.gate == kGateRetry;
+    const double shift = shifted ? retry_shift(rows, d.r) : 0.0;
+    const double* S = reinterpret_cast<const double*>(L.ws + d.oS);
+    double* A = dptr(L, d.oA);
+    double* Y = dptr(L, d.oY);
+    double* Sd = dptr(L, d.oD) + NB * NB;
+    for (int bi = 0; bi < nblk; ++bi)
+      for (int bj = bi; bj < nblk; ++bj)
+        for (int e = threadIdx.x; e < NB * NB; e += kThreads) {
+          const int gi = bi * NB + e / NB, gj = bj * NB + e % NB;
+          double v;
+          if (gi < d.r && gj < d.r) {
+            const int64_t x = static_cast<int64_t>(min(gi, gj)) * rp + max(gi, gj);
+            v = 0.0;
+            for (int sp = 0; sp < ci.splits; ++sp) v += S[sp * plane + x];
+          } else {
+            v = gi == gj ? 1.0 : 0.0;
+          }
+          if (gi == gj) {
+            Sd[gi] = v;
+            if (gi < d.r) v += shift * v;
+          }
+          A[gi * rp + gj] = v;
+        }
+    __syncthreads();
+    const double tol = shifted ? 0.5 * shift : second_tol(d.r);
+    bool failed = false;
+    for (int kb = 0; kb < nblk; ++kb) {
+      bool small;
+      if (!diag_block(L, d, kb, tol, small, nullptr)) {
+        failed = true;
+        break;
+      }
+      __syncthreads();
+      const int64_t o = static_cast<int64_t>(kb) * NB;
+      const int right = nblk - kb - 1;
+      // panel: T_kj = Dinv^T A_kj (j > kb), Y_kc = Dinv^T Y_kc (c < kb)
+      for (int b = 0; b < right + kb; ++b) {
+        double* blk = b < right ? A + o * rp + (kb + 1 + b) * NB : Y + o * rp + (b - right) * NB;
+        f64x4 acc[2][2];
+        block_tn(dptr(L, d.oD), NB, blk, rp, acc);
+        __syncthreads();   // every wavefront has read the block before any writes it
+        gptr<double> out = to_global(blk);
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) out[block_off(fm, fn, v, rp)] = acc[fm][fn][v];
+      }
+      __syncthreads();
+      // trailing: A_ij -= T_ki^T T_kj (kb < i <= j); Y_ic -= T_ki^T Y_kc
+      // (c <= kb, a first write at c = kb)
+      for (int i = kb + 1; i < nblk; ++i) {
+        const double* left = A + o * rp + i * NB;
+        for (int j = 0; j < nblk - i + kb + 1; ++j) {
+          const bool on_a = j < nblk - i;
+          const int c = j - (nblk - i);
+          const double* rgt = on_a ? A + o * rp + (i + j) * NB : Y + o * rp + c * NB;
+          double* outp = on_a ? A + static_cast<int64_t>(i) * NB * rp + (i + j) * NB
+                              : Y + static_cast<int64_t>(i) * NB * rp + c * NB;
+          const bool assign = !on_a && c == kb;
+          f64x4 acc[2][2];
+          block_tn(left, rp, rgt, rp, acc);
+          gptr<double> q = to_global(outp);
+#pragma unroll
+          for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const int64_t e = block_off(fm, fn, v, rp);
+                q[e] = assign ? -acc[fm][fn][v] : q[e] - acc[fm][fn][v];
+              }
+        }
+      }
+      __syncthreads();
+    }
+    if (failed && threadIdx.x == 0) atomicOr(&L.status[d.slot], L.flag);
+    __syncthreads();   // the next work item reuses the shared buffers
+  }
+}
+
+// Q1 = Q T^{-1} with float64 products and sums, rounded once to float32:
+// both triangular multiplies of a two-pass orth (gate kGateTwo).  T^{-1} is
+// upper triangular with a positive diagonal, so Q1 has exactly the Q factor
+// of Q; computed this way Q1 differs from the exact product only by one
+// float32 rounding per entry, and the Q factor the second pass extracts is
+// accurate to about that rounding times Q1's (small) condition number,
+// however ill-conditioned Q was.  64 x 64 output tiles, 2 x 2 wavefronts of 32 x 32
+// on the 16 x 16 x 4 float64 MFMA; each lane loads its own operands
+// (lane l: row l % 16 of the A fragment and column l % 16 of the B
+// fragment at reduction step l / 16), bounds-checked.  T^{-1}[k][j] =
+// Y[j][k] for k <= j (Y = T^{-T} lower triangular; its upper part is not
+// read).  Work items taken in a loop (the launch may have fewer workgroups).
+__global__ __launch_bounds__(kThreads) void k_trmm64(Launch L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  for (int t = blockIdx.x; t < L.total; t += gridDim.x) {
+    MatDesc d;
+    ClassInfo ci;
+    int local;
+    locate(L, t, d, ci, local);
+    if (skipped(L, d)) continue;
+    const int rows = L.which == 0 ? d.m : d.n;
+    const int tm = local / ci.ty, tn = local - (local / ci.ty) * ci.ty;
+    gptr<const float> Q = to_global(orth_src(L, d));
+    gptr<float> dst = to_global(orth_dst(L, d));
+    gptr<const double> Yp = to_global(static_cast<const double*>(dptr(L, d.oY)));
+    const int r = d.r;
+    const int64_t rp = d.rp;
+    const int row0 = tm * NB + (wave >> 1) * 32, col0 = tn * NB + (wave & 1) * 32;
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const int kend = min(r, (tn + 1) * NB);
+    for (int k0 = 0; k0 < kend; k0 += 4) {
+      const int k = k0 + g;
+      double a[2], b[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int row = row0 + 16 * f + c16, col = col0 + 16 * f + c16;
+        a[f] = row < rows && k < r ? static_cast<double>(Q[static_cast<int64_t>(row) * r + k]) : 0.0;
+        b[f] = col < r && k <= col ? Yp[col * rp + k] : 0.0;
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+    }
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = row0 + 16 * fm + g + 4 * v, col = col0 + 16 * fn + c16;
+          if (row < rows && col < r) dst[static_cast<int64_t>(row) * r + col] = static_cast<float>(acc[fm][fn][v]);
+        }
+  }
+}
+
 template <class K>
 hipError_t go(K kernel, const Launch& L, hipStream_t st) {
   if (L.total <= 0) return hipSuccess;
   hipLaunchKernelGGL(kernel, dim3(L.total), dim3(kThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+// Kernels that take their work items in a loop: at most kGatedGrid
+// workgroups, so that a launch in which every matrix is skipped costs little.
+template <class K>
+hipError_t go_capped(K kernel, const Launch& L, hipStream_t st) {
+  if (L.total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(gated_grid(L.total)), dim3(kThreads), 0, st, L);
   return hipGetLastError();
 }
 
@@ -343,5 +619,7 @@ hipError_t launch_chol_init(const Launch& L, hipStream_t st) { return go(k_chol_
 hipError_t launch_chol_diag(const Launch& L, hipStream_t st) { return go(k_chol_diag, L, st); }
 hipError_t launch_chol_panel(const Launch& L, hipStream_t st) { return go(k_chol_panel, L, st); }
 hipError_t launch_chol_trail(const Launch& L, hipStream_t st) { return go(k_chol_trail, L, st); }
+hipError_t launch_chol_one(const Launch& L, hipStream_t st) { return go_capped(k_chol_one, L, st); }
+hipError_t launch_trmm64(const Launch& L, hipStream_t st) { return go_capped(k_trmm64, L, st); }
 
 }  // namespace dion

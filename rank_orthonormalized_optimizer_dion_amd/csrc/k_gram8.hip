@@ -37,14 +37,6 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 // of magnitude <= 64 per row, 65536 * 5 * 4096 < 2^31.
 constexpr int kQFlushSteps = 2048;
 
-__device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
-  return L.status[d.slot] != 0;
-}
-
-__device__ __forceinline__ const float* q_source(const Launch& L, const MatDesc& d) {
-  return reinterpret_cast<const float*>(L.ws + (L.which == 0 ? d.oP : d.oW));
-}
-
 __device__ __forceinline__ int rows_max(const MatDesc& d) { return d.m > d.n ? d.m : d.n; }
 
 // Work item (slice sp, 256-column group cg): the largest |q| bit pattern
@@ -63,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void k_qmax(Launch L) {
   const int rows = L.which == 0 ? d.m : d.n;
   const int groups = (d.r + 255) / 256;
   const int sp = local / groups, cg = local - sp * groups;
-  gptr<const uint32_t> Q = to_global(reinterpret_cast<const uint32_t*>(q_source(L, d)));
+  gptr<const uint32_t> Q = to_global(reinterpret_cast<const uint32_t*>(orth_src(L, d)));
   const int lane = threadIdx.x & 63, rg = threadIdx.x >> 6;
   int cc[4];
 #pragma unroll
@@ -133,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void k_qslice(Launch L) {
   if (!bad && mx != 0) frexpf(__uint_as_float(mx), &e);   // max |q| < 2^e
   if (kb == 0 && h == 0)
     reinterpret_cast<int*>(L.ws + d.oQ + q_exp_off(rmax, d.r))[col] = bad ? kQBadExp : e;
-  gptr<const float> Q = to_global(q_source(L, d));
+  gptr<const float> Q = to_global(orth_src(L, d));
   uint32_t w[kQDigits][4];
 #pragma unroll
   for (int t = 0; t < kQDigits; ++t)

@@ -18,10 +18,6 @@ namespace {
 
 constexpr int kElemsPerTile = 4 * kThreads;
 
-__device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
-  return L.status[d.slot] != 0;
-}
-
 // which = 0: P (m x r) from the M V partials; 1: W (n x r) from the M^T U
 // partials.
 __global__ __launch_bounds__(kThreads) void k_reduce(Launch L) {

@@ -26,6 +26,10 @@ hipError_t launch_chol_init(const Launch& L, hipStream_t st);
 hipError_t launch_chol_diag(const Launch& L, hipStream_t st);
 hipError_t launch_chol_panel(const Launch& L, hipStream_t st);
 hipError_t launch_chol_trail(const Launch& L, hipStream_t st);
+// the whole factorization of each matrix in one workgroup (shifted retry,
+// second pass) and the float64 triangular multiply that follows it
+hipError_t launch_chol_one(const Launch& L, hipStream_t st);
+hipError_t launch_trmm64(const Launch& L, hipStream_t st);
 
 hipError_t launch_reduce(const Launch& L, hipStream_t st);
 hipError_t launch_colnorm(const Launch& L, hipStream_t st);

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) >= 12
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.dion_version() >= 100
+    assert lib.dion_version() >= 200
 
 
 def test_only_dion_symbols_exported():
@@ -126,6 +126,13 @@ def test_shard_entry_points_reject_null_plan(lib):
         dion.ERR_INVALID_ARG
 
 
+def test_plan_buffer_rejects_bad_arguments(lib):
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    for which in (dion.BUF_P, dion.BUF_U, dion.BUF_W):
+        assert lib.dion_plan_buffer(None, which, 0, ctypes.byref(off), ctypes.byref(nb)) == \
+            dion.ERR_INVALID_ARG
+
+
 def test_gram_variant_bit(lib):
     # the sliced Gram (default) needs its digit planes in the workspace;
     # DION_GRAM_F64 does not, and an unknown bit is rejected
@@ -149,6 +156,8 @@ def test_binding_constants_match_header():
     assert defs["DION_GRAM_F64"] == dion.GRAM_F64
     assert defs["DION_SHARDED"] == dion.SHARDED
     assert defs["DION_SHARD_GRAM"] == dion.SHARD_GRAM and defs["DION_SHARD_W"] == dion.SHARD_W
+    assert (defs["DION_BUF_P"], defs["DION_BUF_U"], defs["DION_BUF_W"]) == \
+        (dion.BUF_P, dion.BUF_U, dion.BUF_W)
     assert defs["DION_OK"] == dion.OK and defs["DION_ERR_INVALID_ARG"] == dion.ERR_INVALID_ARG
     assert defs["DION_ERR_WORKSPACE"] == dion.ERR_WORKSPACE and defs["DION_ERR_HIP"] == dion.ERR_HIP
     assert defs["DION_ERR_BREAKDOWN"] == dion.ERR_BREAKDOWN

@@ -8,5 +8,6 @@ from .configs import (  # noqa: F401
     CONFIGS, MatrixSpec, Workload, config, stack_160m, stack_3b,
 )
 from .generators import (  # noqa: F401
-    MatrixStream, bf16_bits_to_f32, f32_to_bf16_bits, random_orthonormal, rng,
+    MatrixStream, bf16_bits_to_f32, conditioned_inputs, f32_to_bf16_bits,
+    random_orthonormal, rng,
 )

@@ -142,3 +142,40 @@ class MatrixStream:
         if self.wl.g_dtype == "bf16":
             return bf16_bits_to_f32(g).astype(np.float64)
         return g.astype(np.float64)
+
+
+def conditioned_inputs(m: int, n: int, r: int, kappa: float, seed: int,
+                       g_dtype: str = "f32", side: str = "P",
+                       duplicate: Optional[int] = None):
+    """One matrix whose factor P = M V (side "P") or W = M^T U (side "W")
+    has nearly collinear columns and a condition number of about kappa:
+    M = A diag(s) B^T with A (m x k), B (n x k) random orthonormal,
+    k = min(r + 8, m, n), s log-spaced from 1 down to 1/kappa over the first
+    r directions and 1/(10 kappa) on the rest; R0 = 0, X0 = 0.02 N(0,1).
+    Side "P": V0 random orthonormal, so every column of P mixes all the
+    directions.  Side "W": V0 = B_r diag(1/s) Z (Z random orthonormal r x r)
+    with each column scaled to unit length, so P = A_r Z D is well-
+    conditioned and U = orth(P) mixes the directions evenly, and W = B_r
+    diag(s) Z' is the ill-conditioned factor.  duplicate = j makes column
+    j + 1 of V0 a copy of column j (P then has two equal columns).  Returns
+    (X0, G, R0, V0) as the library receives them (G float32 or bfloat16
+    bits)."""
+    g = rng(seed, 0, 0)
+    k = min(r + 8, m, n)
+    A = random_orthonormal(g, m, k)
+    B = random_orthonormal(g, n, k)
+    s = np.full(k, 0.1 / kappa)
+    s[:min(r, k)] = np.logspace(0.0, -np.log10(kappa), min(r, k))
+    G = ((A * s) @ B.T).astype(np.float32)
+    if side == "W":
+        Z = random_orthonormal(g, r, r)
+        V = (B[:, :r] / s[:r]) @ Z
+        V /= np.linalg.norm(V, axis=0)
+    else:
+        V = random_orthonormal(g, n, r)
+    if duplicate is not None:
+        V[:, duplicate + 1] = V[:, duplicate]
+    X = (0.02 * g.standard_normal((m, n))).astype(np.float32)
+    if g_dtype == "bf16":
+        G = f32_to_bf16_bits(G)
+    return X, G, np.zeros((m, n), dtype=np.float32), V.astype(np.float32)
