@@ -10,8 +10,10 @@ the method).  Inputs are synthetic, drawn on the device before timing.
 Prints one JSON line.  The per-phase durations come from HIP events the
 library records on its own stream during the timed steps; the dominant
 phase (one kernel launch) is reported against the MI355X roofline.  The
-CPU baseline is the float64 oracle on a bounded sample of the same
-workload (one layer), scaled to the whole stack.
+line also carries the same stack with the other arithmetic of the products
+and at the other rank fraction.  The CPU baseline is the float64 oracle on
+a bounded sample of the same workload (four layers), scaled to the whole
+stack.
 """
 from __future__ import annotations
 
@@ -212,72 +214,111 @@ def roofline_of(phase: str, ms: float, f: dict, b: dict, traffic, math: str):
     return out
 
 
-def cpu_baseline(wl, variant: str, layers: int):
-    """The float64 oracle on the first `layers` layer(s) of the stack (one
-    step per matrix, inputs from the seeded numpy streams), scaled to the
-    whole stack."""
-    import numpy as np
-    from oracle import dion_step
-    from workloads import MatrixStream
-    blas = "unknown BLAS"
+def _blas_info():
+    blas, threads = "unknown BLAS", len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        threads = max((i.get("num_threads", 1) for i in libs), default=1)
+        threads = max((i.get("num_threads", 1) for i in libs), default=threads)
         if libs:
             blas = f"{libs[0].get('internal_api', 'blas')} {libs[0].get('version', '')}".strip()
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        pass
     cpu = "unknown CPU"
     try:
         with open("/proc/cpuinfo") as fh:
             cpu = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
     except (OSError, StopIteration):
         pass
-    per_layer = sum(1 for s in wl.mats if s.layer == 0)
-    sample = [s for s in wl.mats if s.layer < layers]
+    return blas, int(threads), cpu
+
+
+def oracle_seconds(wl, variant: str, indices, steps: int = 1, threads=None) -> float:
+    """Seconds the float64 oracle takes for `steps` steps of the matrices
+    `indices` of workload `wl` (inputs from the seeded numpy streams, drawn
+    outside the timing); threads = None uses every BLAS thread."""
+    import contextlib
+    import numpy as np
+    from oracle import dion_step
+    from workloads import MatrixStream
+    limit = contextlib.nullcontext()
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=threads, user_api="blas")
+    eta, beta = float(np.float32(wl.eta)), float(np.float32(wl.beta))
     total = 0.0
-    for s in sample:
-        st = MatrixStream(wl, s)
-        x, r, v = (a.astype(np.float64) for a in st.init())
-        g = st.grad_f64(0)
-        t0 = time.perf_counter()
-        dion_step(x, g, r, v, float(np.float32(wl.eta)), float(np.float32(wl.beta)), variant)
-        total += time.perf_counter() - t0
+    with limit:
+        for i in indices:
+            st = MatrixStream(wl, wl.mats[i])
+            x, r, v = (a.astype(np.float64) for a in st.init())
+            for t in range(steps):
+                g = st.grad_f64(t)
+                t0 = time.perf_counter()
+                res = dion_step(x, g, r, v, eta, beta, variant)
+                total += time.perf_counter() - t0
+                x, r, v = res.X, res.R, res.V
+    return total
+
+
+def cpu_baseline(wl, variant: str, layers: int):
+    """The float64 oracle on the first `layers` layer(s) of the stack (one
+    step per matrix, inputs from the seeded numpy streams), scaled to the
+    whole stack."""
+    blas, threads, cpu = _blas_info()
+    per_layer = sum(1 for s in wl.mats if s.layer == 0)
+    sample = [s.index for s in wl.mats if s.layer < layers]
+    total = oracle_seconds(wl, variant, sample)
     scale = len(wl.mats) / len(sample)
-    return {"value": round(1.0 / (total * scale), 6), "unit": "steps/s", "cores": int(threads),
+    return {"value": round(1.0 / (total * scale), 6), "unit": "steps/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(sample)} of {len(wl.mats)} matrices (layer 0, {per_layer} roles), "
-                      f"one {variant} step each in numpy float64 ({blas}, {cpu}), {total:.1f} s, "
-                      f"scaled x{scale:g}"}
+            "sample": f"{len(sample)} of {len(wl.mats)} matrices (layers 0-{layers - 1}, "
+                      f"{per_layer} roles each), one {variant} step each in numpy float64 "
+                      f"({blas}, {cpu}), {total:.1f} s, scaled x{scale:g}"}
 
 
 def step_roofline(shapes, variant: str, eg: int, math: str):
-    """Whole-step roofline time: the three products at the chosen
-    arithmetic's matrix peak (ops per flop included), orth at the float32
-    matrix peak, against the compulsory bytes at the HBM peak.  Returns
-    (T_roof, T_mfma, flops, compulsory bytes)."""
-    f, _ = phase_model(shapes, variant, eg)
+    """Whole-step roofline time: T_roof = max(B_min / HBM peak, F_alg /
+    P_used), with every algorithmic flop at the matrix peak of the
+    arithmetic the products run in (P_used = the float32 matrix peak, or a
+    third of the bfloat16 peak for split-bfloat16, three bfloat16 products
+    per float32 product).  Returns (T_roof, T_mfma, flops, compulsory bytes)."""
     flops, bmin = step_model(shapes, variant, eg)
     peak, ops = MATH[math]
-    f_prod = f["mv"] + f["mtu"] + f["update"]
-    t_mfma = ops * f_prod / peak + (flops - f_prod) / MFMA_F32_PEAK
+    t_mfma = ops * flops / peak
     return max(bmin / HBM_PEAK, t_mfma), t_mfma, flops, bmin
 
 
-# the other workloads: (label, config number, rank for config 5, timed steps)
-OTHER_CONFIGS = (("single-256x128", 1, None, 200), ("planted-2048", 2, None, 40),
-                 ("gpt160m-stack", 3, None, 30), ("mlp70b-r512", 5, 512, 10),
-                 ("mlp70b-r2048", 5, 2048, 10))
+def step_roofline_entry(shapes, variant: str, eg: int, math: str, sec: float) -> dict:
+    t_roof, t_mfma, flops, bmin = step_roofline(shapes, variant, eg, math)
+    peak, ops = MATH[math]
+    return {"bound": "mfma" if t_mfma > bmin / HBM_PEAK else "hbm",
+            "p_used_tflops": round(peak / ops / 1e12, 1),
+            "algorithmic_tflop": round(flops / 1e12, 3),
+            "compulsory_gb": round(bmin / 1e9, 3),
+            "effective_gbps": round(bmin / sec / 1e9, 1),
+            "effective_tflops": round(flops / sec / 1e12, 2),
+            "frac": round(t_roof / sec, 4)}
 
 
-def time_configs(dion, torch, dev, math: str):
+# the other workloads: (label, config number, rank for config 5, timed steps,
+# oracle sample: (matrix indices, steps), single-threaded oracle too)
+OTHER_CONFIGS = (("single-256x128", 1, None, 200, ((0,), 10), True),
+                 ("planted-2048", 2, None, 40, ((0,), 3), True),
+                 ("gpt160m-stack", 3, None, 30, (tuple(range(72)), 1), False),
+                 ("mlp70b-r512", 5, 512, 10, ((0,), 1), False),
+                 ("mlp70b-r2048", 5, 2048, 10, ((0,), 1), False))
+
+
+def time_configs(dion, torch, dev, math: str, cpu: bool = True):
     """steps/s of both variants on every other workload, with the fraction
-    of the whole-step roofline each reaches."""
+    of the whole-step roofline each reaches, and the float64 oracle's
+    steps/s on the same workload (all BLAS threads; also one thread for the
+    single matrices)."""
     from workloads import config
     from workloads.device import DeviceMatrix
     out = {}
-    for label, num, r, steps in OTHER_CONFIGS:
+    blas, threads, cpu_name = _blas_info()
+    for label, num, r, steps, (sample, osteps), single in OTHER_CONFIGS:
         wl = config(num, r=r) if r else config(num)
         print(f"[bench] {wl.name}", file=sys.stderr, flush=True)
         mats = [DeviceMatrix(wl, s, dev) for s in wl.mats]
@@ -286,14 +327,22 @@ def time_configs(dion, torch, dev, math: str):
         eg = 2 if wl.g_dtype == "bf16" else 4
         for var in ("orth", "dion"):
             sec, _ = time_plan(dion, torch, mats, var, steps, 3, wl.eta, wl.beta, math)
-            t_roof, t_mfma, flops, bmin = step_roofline(shapes, var, eg, math)
-            out[f"{label}_{var}"] = {
-                "workload": wl.name, "steps_per_s": round(1 / sec, 2),
-                "ms_per_step": round(sec * 1e3, 4),
-                "bound": "mfma" if t_mfma >= bmin / HBM_PEAK else "hbm",
-                "roofline_frac": round(t_roof / sec, 4),
-                "effective_tflops": round(flops / sec / 1e12, 2),
-                "effective_gbps": round(bmin / sec / 1e9, 1)}
+            entry = {"workload": wl.name, "steps_per_s": round(1 / sec, 2),
+                     "ms_per_step": round(sec * 1e3, 4),
+                     "step_roofline": step_roofline_entry(shapes, var, eg, math, sec)}
+            if cpu and var == "orth":
+                scale = len(wl.mats) / len(sample)
+                t = oracle_seconds(wl, var, sample, osteps) * scale / osteps
+                entry["cpu_baseline"] = {"value": round(1.0 / t, 4), "unit": "steps/s",
+                                         "cores": threads, "kind": "oracle",
+                                         "sample": f"{len(sample)} of {len(wl.mats)} matrices, "
+                                                   f"{osteps} step(s), numpy float64 ({blas}, "
+                                                   f"{cpu_name})"}
+                if single:
+                    t1 = oracle_seconds(wl, var, sample, osteps, threads=1) * scale / osteps
+                    entry["cpu_baseline_1thread"] = {"value": round(1.0 / t1, 4),
+                                                     "unit": "steps/s", "cores": 1}
+            out[f"{label}_{var}"] = entry
         del mats
         torch.cuda.empty_cache()
     return out
@@ -311,12 +360,16 @@ def main(argv=None) -> int:
     ap.add_argument("--rank-div", type=int, choices=(4, 16), default=4)
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--extra", action="store_true",
-                    help="also time the other variant and rank fraction")
+                    help="also time the other variant at both rank fractions and one GPU's "
+                         "share of a row-sharded stack")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time only the main setting (no other arithmetic or rank fraction; "
+                         "for profiling runs)")
     ap.add_argument("--configs", action="store_true",
                     help="also time both variants on the other workloads (single matrices, "
                          "the 160M stack, the 70B MLP matrix) under \"configs\"")
-    ap.add_argument("--cpu-layers", type=int, default=1)
+    ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (a known byte "
                          "count for scaling hardware traffic counters)")
@@ -364,7 +417,6 @@ def main(argv=None) -> int:
     traffic = measured_traffic(kernel, wl.name) if kernel.startswith("k_") else None
     roof = roofline_of(dom, phases[dom], f, b, traffic, args.math)
     roof["kernel"] = kernel
-    t_roof, t_mfma, flops, bmin = step_roofline(shapes, args.variant, eg, args.math)
     out = {
         "metric": "Dion/Orth-Dion steps/sec + effective HBM GB/s (% roofline), 3B-shaped stack",
         "value": round(1.0 / sec, 4),
@@ -383,28 +435,31 @@ def main(argv=None) -> int:
                    "g_dtype": "bf16", "state_dtype": "f32", "layers": args.layers,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
-        "step_roofline": {
-            "bound": "mfma" if t_mfma > bmin / HBM_PEAK else "hbm",
-            "algorithmic_tflop": round(flops / 1e12, 3),
-            "compulsory_gb": round(bmin / 1e9, 3),
-            "effective_gbps": round(bmin / sec / 1e9, 1),
-            "effective_tflops": round(flops / sec / 1e12, 2),
-            "frac": round(t_roof / sec, 4),
-        },
+        "step_roofline": step_roofline_entry(shapes, args.variant, eg, args.math, sec),
         "phase_ms": {k: round(v, 3) for k, v in phases.items()},
     }
+    if args.main_only:
+        print(json.dumps(out), flush=True)
+        return 0
+    # the same stack with the other arithmetic and at the other rank
+    # fraction, in the default line too (fewer timed steps)
+    other_math = "f32" if args.math == "bf16x3" else "bf16x3"
+    sec_m, ph_m = time_plan(dion, torch, mats, args.variant, max(3, args.steps // 2), 1,
+                            wl.eta, wl.beta, other_math)
+    out[f"{other_math}_products"] = {
+        "steps_per_s": round(1 / sec_m, 4),
+        "step_roofline_frac": step_roofline_entry(shapes, args.variant, eg, other_math, sec_m)["frac"],
+        "p_used_tflops": round(MATH[other_math][0] / MATH[other_math][1] / 1e12, 1),
+        "phase_ms": {k: round(v, 3) for k, v in ph_m.items()}}
+    extra = {}
     if args.extra:
-        extra = {}
-        other_math = "f32" if args.math == "bf16x3" else "bf16x3"
-        secm, phm = time_plan(dion, torch, mats, args.variant, max(3, args.steps // 2), 1, wl.eta,
-                              wl.beta, other_math)
-        extra[f"{args.variant}_r1/{args.rank_div}_{other_math}"] = {
-            "steps_per_s": round(1 / secm, 4), "phase_ms": {k: round(v, 3) for k, v in phm.items()}}
         other = "dion" if args.variant == "orth" else "orth"
         sec2, ph2 = time_plan(dion, torch, mats, other, max(3, args.steps // 2), 1, wl.eta,
                               wl.beta, args.math)
-        extra[f"{other}_r1/{args.rank_div}"] = {"steps_per_s": round(1 / sec2, 4),
-                                                "phase_ms": {k: round(v, 3) for k, v in ph2.items()}}
+        extra[f"{other}_r1/{args.rank_div}"] = {
+            "steps_per_s": round(1 / sec2, 4),
+            "step_roofline_frac": step_roofline_entry(shapes, other, eg, args.math, sec2)["frac"],
+            "phase_ms": {k: round(v, 3) for k, v in ph2.items()}}
         # one GPU's share of an 8-way row-sharded (FSDP) stack: rows
         # [0, m/8) of every matrix, stepped in the three DION_SHARDED stages
         whole = [(d.X, d.G, d.R, d.V) for d in mats]
@@ -415,17 +470,28 @@ def main(argv=None) -> int:
         extra[f"{args.variant}_r1/{args.rank_div}_shard1of8"] = {
             "steps_per_s": round(1 / sec4, 4), "rows": "m/8 of every matrix",
             "exchange": "the all-reduced Gram matrix and W landed by device copies"}
-        del shard
-        div2 = 16 if args.rank_div == 4 else 4
-        wl2 = config(4, div2, layers=args.layers)
-        for d, s in zip(mats, wl2.mats):
-            d.reset_rank(s.r)
-        torch.cuda.synchronize()
-        for var in ("orth", "dion"):
-            sec3, ph3 = time_plan(dion, torch, mats, var, max(3, args.steps // 2), 1, wl.eta,
-                                  wl.beta, args.math)
-            extra[f"{var}_r1/{div2}"] = {"steps_per_s": round(1 / sec3, 4),
-                                         "phase_ms": {k: round(v, 3) for k, v in ph3.items()}}
+        del shard, whole
+    # the other rank fraction, in the default line too
+    div2 = 16 if args.rank_div == 4 else 4
+    wl2 = config(4, div2, layers=args.layers)
+    for d, s2 in zip(mats, wl2.mats):
+        d.reset_rank(s2.r)
+    torch.cuda.synchronize()
+    shapes2 = [(s2.m, s2.n, s2.r) for s2 in wl2.mats]
+    sec_r, ph_r = time_plan(dion, torch, mats, args.variant, args.steps, 1, wl.eta, wl.beta,
+                            args.math)
+    out[f"{args.variant}_r1/{div2}"] = {
+        "steps_per_s": round(1 / sec_r, 4),
+        "step_roofline": step_roofline_entry(shapes2, args.variant, eg, args.math, sec_r),
+        "phase_ms": {k: round(v, 3) for k, v in ph_r.items()}}
+    if args.extra:
+        other = "dion" if args.variant == "orth" else "orth"
+        sec3, ph3 = time_plan(dion, torch, mats, other, max(3, args.steps // 2), 1, wl.eta,
+                              wl.beta, args.math)
+        extra[f"{other}_r1/{div2}"] = {
+            "steps_per_s": round(1 / sec3, 4),
+            "step_roofline_frac": step_roofline_entry(shapes2, other, eg, args.math, sec3)["frac"],
+            "phase_ms": {k: round(v, 3) for k, v in ph3.items()}}
         out["extra"] = extra
     del mats
     torch.cuda.empty_cache()

@@ -75,47 +75,75 @@ __device__ __forceinline__ bool skipped(const Launch& L, const MatDesc& d) {
   }
 }
 
-// The factors of orth(): pass 1 reads Q0 = P (which = 0) or W (which = 1);
-// the result is U (workspace oB) or Vbar (written into V).  When a second
-// pass follows (kCtlTwo), the first writes oC and the second reads it.
-__device__ __forceinline__ const float* orth_src(const Launch& L, const MatDesc& d) {
-  if (L.pass == 2) return reinterpret_cast<const float*>(L.ws + d.oC);
+// A wave-uniform 64-bit field of a matrix descriptor as a plain value: a
+// choice among several fields then stays a choice among values, where a
+// choice among the fields themselves would become a load at a computed
+// address and keep the whole descriptor copy in private memory.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// The factor the first CholeskyQR pass reads: P (which = 0) or W
+// (which = 1), and where a single-pass orth leaves its result: U (workspace
+// oB) or Vbar (written into V).
+__device__ __forceinline__ const float* first_src(const Launch& L, const MatDesc& d) {
   return reinterpret_cast<const float*>(L.ws + (L.which == 0 ? d.oP : d.oW));
 }
-__device__ __forceinline__ float* orth_dst(const Launch& L, const MatDesc& d) {
-  if (L.pass == 1 && (L.status[d.slot] & kCtlTwo)) return reinterpret_cast<float*>(L.ws + d.oC);
+__device__ __forceinline__ float* final_dst(const Launch& L, const MatDesc& d) {
   return L.which == 0 ? reinterpret_cast<float*>(L.ws + d.oB) : d.V;
 }
 
-// Whether orth() of matrix d needs more than its first CholeskyQR pass,
-// decided once the first pass's Cholesky factorization is complete: 0 (one
-// pass), kCtlTwo (a second pass) or kCtlTwo | kCtlRetry (the first pass
-// again with a shift, then the second).  One pass leaves Q T^{-1} with an
-// orthogonality error of about lambda_min(C)^-1 times the Gram matrix's
-// relative error (C the column-scaled Gram matrix); t = trace(C^{-1}) lies
-// between 1 / lambda_min(C) and r / lambda_min(C), so t <= kTraceTwo r keeps
-// that error at float32's level (the workloads here stay below 2 r), and
-// t > kTraceRetry r means the first pass's result is too far from
-// orthonormal for a second pass to repair.  The chain's kernels leave t in
-// per-block partial sums (see k_chol.hip) and the diagonal steps may
-// already have asked for more (small pivot ratios, control bits); every
-// workgroup that asks sums the partials in the same order, so all of them
-// reach the same answer.  Plans without retries (row-sharded P) always
-// take one pass.
-constexpr double kTraceTwo = 1e3;
-constexpr double kTraceRetry = 1e7;
-__device__ __forceinline__ int32_t orth_decision(const Launch& L, const MatDesc& d) {
-  if (!L.retry) return 0;
-  const int32_t s = L.status[d.slot];
-  if (s & kCtlRetry) return kCtlTwo | kCtlRetry;
-  const int nblk = d.rp / kCholNB;
-  const double* part = reinterpret_cast<const double*>(L.ws + d.oD) + kCholNB * kCholNB + d.rp;
-  double t = 0.0;
-  for (int jb = 0; jb < nblk; ++jb)
-    for (int c = 0; c <= jb; ++c) t += part[jb * nblk + c];
-  if (!(t <= kTraceRetry * d.r)) return kCtlTwo | kCtlRetry;
-  if (!(t <= kTraceTwo * d.r) || (s & kCtlTwo)) return kCtlTwo;
-  return 0;
+// The factors of the kernels that also serve a two-pass orth: pass 1 reads
+// the first pass's factor; when a second pass follows (kCtlTwo), the first
+// writes oC and the second reads it and writes the final result.
+__device__ __forceinline__ const float* orth_src(const Launch& L, const MatDesc& d) {
+  const int64_t off = L.pass == 2 ? uniform64(d.oC) : L.which == 0 ? uniform64(d.oP) : uniform64(d.oW);
+  return reinterpret_cast<const float*>(L.ws + off);
+}
+__device__ __forceinline__ float* orth_dst(const Launch& L, const MatDesc& d) {
+  const bool to_c = L.pass == 1 && (L.status[d.slot] & kCtlTwo);
+  const int64_t ws = reinterpret_cast<int64_t>(L.ws);
+  const int64_t a = to_c ? ws + uniform64(d.oC)
+                         : L.which == 0 ? ws + uniform64(d.oB)
+                                        : uniform64(reinterpret_cast<int64_t>(d.V));
+  return reinterpret_cast<float*>(a);
+}
+
+// Runs body(d, ci, local) over this workgroup's share of the launch's work
+// items, for kernels launched with fewer workgroups than items (the gated
+// launches of orth's extra passes): workgroup b takes one contiguous chunk
+// of items, so a matrix the gate excludes is passed over with one look at
+// its status word, not one per item.  With one workgroup per item it takes
+// item xcd_remap(b) like every other kernel.  The body must be uniform over
+// the workgroup (it may contain barriers).
+template <class F>
+__device__ __forceinline__ void for_items(const Launch& L, F&& body) {
+  if (static_cast<int>(gridDim.x) >= L.total) {
+    MatDesc d;
+    ClassInfo ci;
+    int local;
+    locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+    if (!skipped(L, d)) body(d, ci, local);
+    return;
+  }
+  const int per = (L.total + gridDim.x - 1) / gridDim.x;
+  int t = blockIdx.x * per;
+  const int tend = min(L.total, t + per);
+  while (t < tend) {
+    MatDesc d;
+    ClassInfo ci;
+    int local;
+    locate(L, t, d, ci, local);
+    const int stop = min(tend, t - local + ci.tiles);   // the next matrix's first item
+    if (skipped(L, d)) {
+      t = stop;
+      continue;
+    }
+    for (; t < stop; ++t, ++local) body(d, ci, local);
+  }
 }
 
 // Workgroups of a launch whose kernel loops over its work items: launches

@@ -253,9 +253,6 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     };
     d.oP = take(m * r * 4);
     d.oB = take(m * r * 4);
-    // first-pass output of a two-pass orth: of P (m rows), and of W (n
-    // rows) for Orth-Dion
-    d.oC = take((p.variant == DION_VARIANT_ORTH ? std::max(m, n) : m) * r * 4);
     d.oW = take(n * r * 4);
     d.oS = take(static_cast<size_t>(std::max(k.s_gp, k.s_gw)) * rp * rp * 8);
     d.oA = take(rp * rp * 8);
@@ -269,6 +266,10 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     d.oH = p.math ? take(r * std::max(plane_pitch(k.m), plane_pitch(k.n)) * 4) : 0;
     d.oE = k.bn_n == 256 ? take((m + 2 * n) * plane_pitch(k.r) * 4) : 0;
     d.oQ = p.gram8 ? take(static_cast<size_t>(q_bytes(std::max(k.m, k.n), k.r))) : 0;
+    // first-pass output of a two-pass orth: of P (m rows), and of W (n
+    // rows) for Orth-Dion; last, so that the buffers every step uses keep
+    // the offsets they have without it
+    d.oC = take((p.variant == DION_VARIANT_ORTH ? std::max(m, n) : m) * r * 4);
     p.table[g] = d;
   }
   p.ws_bytes = off;
@@ -467,8 +468,13 @@ hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
       return true;
     }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
   }
-  // the float32 triangular multiply of single-pass matrices; its
-  // workgroups also decide, per matrix, whether a second pass is needed
+  if (base.retry) {   // the decision whether more passes follow
+    DION_TRY(grouped(p, base, [&](const ClassRec&, ClassInfo& ci) {
+      ci.tiles = 1;
+      return true;
+    }, [&](const Launch& L) { return launch_orth_decide(L, st); }));
+  }
+  // the float32 triangular multiply of single-pass matrices
   base.gate = kGateOne;
   for (int bn : {128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {

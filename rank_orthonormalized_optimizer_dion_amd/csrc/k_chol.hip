@@ -40,7 +40,7 @@ constexpr int NB = kCholNB;
 // the first pass for the shifted retry; below kRatioTwo it asks for a
 // second pass.  The finer decision comes from the trace of C^{-1} (C the
 // column-scaled Gram matrix), which the chain gathers in per-block partial
-// sums (orth_decision in device_common.h).  Plans whose first pass cannot
+// sums and k_orth_decide adds up.  Plans whose first pass cannot
 // be repeated (the row-sharded P, whose Gram matrix is summed by the
 // caller) treat a ratio below kRatioTwo as a breakdown.
 constexpr double kRatioTwo = 1e-6;
@@ -435,6 +435,45 @@ __global__ __launch_bounds__(kThreads, 4) void k_chol_trail(Launch L) {
       }
 }
 
+// Whether orth() of each matrix needs more than its first CholeskyQR pass,
+// decided once the first pass's factorization is complete (one workgroup
+// per matrix, after the chain, for plans whose first pass may be followed
+// by more).  One pass leaves Q T^{-1} with an orthogonality error of about
+// lambda_min(C)^-1 times the Gram matrix's relative error (C the column-
+// scaled Gram matrix).  t = trace(C^{-1}) lies between 1 / lambda_min(C)
+// and r / lambda_min(C): t <= kTraceTwo r keeps that error at float32's
+// level (the workloads here stay below 2 r), and t > kTraceRetry r means
+// the first pass's result is too far from orthonormal for a second pass to
+// repair.  The chain left t in per-block partial sums; they are added in a
+// fixed order (a strided sum per thread, then block_sum), so the decision
+// does not depend on timing.  Sets kCtlTwo, or kCtlTwo | kCtlRetry, in the
+// status word; the diagonal steps may have set them already (small or
+// failed pivots).
+constexpr double kTraceTwo = 1e3;
+constexpr double kTraceRetry = 1e7;
+
+__global__ __launch_bounds__(kThreads) void k_orth_decide(Launch L) {
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  const int nblk = d.rp / NB;
+  const double* part = dptr(L, d.oD) + NB * NB + d.rp;
+  double t = 0.0;
+  for (int e = threadIdx.x; e < nblk * nblk; e += kThreads) {
+    const int jb = e / nblk, c = e - jb * nblk;
+    if (c <= jb) t += part[e];
+  }
+  t = block_sum(t);
+  if (threadIdx.x == 0) {
+    int32_t more = 0;
+    if (!(t <= kTraceRetry * d.r)) more = kCtlTwo | kCtlRetry;
+    else if (!(t <= kTraceTwo * d.r)) more = kCtlTwo;
+    if (more) atomicOr(&L.status[d.slot], more);
+  }
+}
+
 // The whole factorization of one matrix in one workgroup (the shifted
 // retry of the first pass, gate kGateRetry, and the second pass, gate
 // kGateTwo with pass 2): A from the Gram partials (plus s diag(S) for the
@@ -443,12 +482,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_chol_trail(Launch L) {
 // the chain's kernels.  A failed pivot is a breakdown.  Work items: one per matrix,
 // taken in a loop so that a launch with few workgroups covers any list.
 __global__ __launch_bounds__(kThreads) void k_chol_one(Launch L) {
-  for (int t = blockIdx.x; t < L.total; t += gridDim.x) {
-    MatDesc d;
-    ClassInfo ci;
-    int local;
-    locate(L, t, d, ci, local);
-    if (skipped(L, d)) continue;
+  for_items(L, [&](const MatDesc& d, const ClassInfo& ci, int) {
     const int rows = L.which == 0 ? d.m : d.n;
     const int nblk = d.rp / NB;
     const int64_t rp = d.rp, plane = rp * rp;
@@ -532,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void k_chol_one(Launch L) {
     }
     if (failed && threadIdx.x == 0) atomicOr(&L.status[d.slot], L.flag);
     __syncthreads();   // the next work item reuses the shared buffers
-  }
+  });
 }
 
 // Q1 = Q T^{-1} with float64 products and sums, rounded once to float32:
@@ -546,16 +580,11 @@ __global__ __launch_bounds__(kThreads) void k_chol_one(Launch L) {
 // (lane l: row l % 16 of the A fragment and column l % 16 of the B
 // fragment at reduction step l / 16), bounds-checked.  T^{-1}[k][j] =
 // Y[j][k] for k <= j (Y = T^{-T} lower triangular; its upper part is not
-// read).  Work items taken in a loop (the launch may have fewer workgroups).
+// read).  Work items as for_items hands them out.
 __global__ __launch_bounds__(kThreads) void k_trmm64(Launch L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  for (int t = blockIdx.x; t < L.total; t += gridDim.x) {
-    MatDesc d;
-    ClassInfo ci;
-    int local;
-    locate(L, t, d, ci, local);
-    if (skipped(L, d)) continue;
+  for_items(L, [&](const MatDesc& d, const ClassInfo& ci, int local) {
     const int rows = L.which == 0 ? d.m : d.n;
     const int tm = local / ci.ty, tn = local - (local / ci.ty) * ci.ty;
     gptr<const float> Q = to_global(orth_src(L, d));
@@ -594,7 +623,7 @@ __global__ __launch_bounds__(kThreads) void k_trmm64(Launch L) {
           const int row = row0 + 16 * fm + g + 4 * v, col = col0 + 16 * fn + c16;
           if (row < rows && col < r) dst[static_cast<int64_t>(row) * r + col] = static_cast<float>(acc[fm][fn][v]);
         }
-  }
+  });
 }
 
 template <class K>
@@ -620,6 +649,7 @@ hipError_t launch_chol_diag(const Launch& L, hipStream_t st) { return go(k_chol_
 hipError_t launch_chol_panel(const Launch& L, hipStream_t st) { return go(k_chol_panel, L, st); }
 hipError_t launch_chol_trail(const Launch& L, hipStream_t st) { return go(k_chol_trail, L, st); }
 hipError_t launch_chol_one(const Launch& L, hipStream_t st) { return go_capped(k_chol_one, L, st); }
+hipError_t launch_orth_decide(const Launch& L, hipStream_t st) { return go(k_orth_decide, L, st); }
 hipError_t launch_trmm64(const Launch& L, hipStream_t st) { return go_capped(k_trmm64, L, st); }
 
 }  // namespace dion

@@ -246,10 +246,9 @@ __global__ __launch_bounds__(kThreads) void k_mtu(Launch L) {
 // float64 and the sums are float64, so S is accurate enough for a single
 // CholeskyQR pass.
 template <int BG, bool VEC, bool FULL>
-__device__ __forceinline__ void gram_body(const Launch& L, const MatDesc& d, int s, int ti, int tj,
-                                          int kbeg, int kend, f32x4* smem) {
+__device__ __forceinline__ void gram_body(const Launch& L, const MatDesc& d, const float* Q, int s,
+                                          int ti, int tj, int kbeg, int kend, f32x4* smem) {
   constexpr int BK = 32, FB = BG / 32;
-  const float* Q = orth_src(L, d);
   LoadXC<BG, BK, VEC, SrcF32> la(SrcF32{Q}, d.r, ti * BG, d.r, kend);
   LoadXC<BG, BK, VEC, SrcF32> lb(SrcF32{Q}, d.r, tj * BG, d.r, kend);
   f64x4 acc[FB][FB];
@@ -288,37 +287,55 @@ __device__ __forceinline__ void gram_body(const Launch& L, const MatDesc& d, int
 
 // Four blocks per CU (at most 128 registers per lane): the float64 MFMAs
 // are long, and the extra wavefronts cover the tile loads and barriers.
-// Work items are taken in a loop: the launches of the second pass and of
-// the shifted retry (gated, see dion_types.h) run fewer workgroups than
-// items; the others one workgroup per item.
+// Work item `local` of a Gram launch: tile (ti, tj) of the upper triangle
+// and reduction slice s.
+template <int BG, bool VEC>
+__device__ __forceinline__ void gram_item(const Launch& L, const MatDesc& d, const float* Q,
+                                          const ClassInfo& ci, int local, f32x4* smem) {
+  constexpr int BK = 32;
+  const int rows = L.which == 0 ? d.m : d.n;
+  const int nt = ci.tx;
+  const int pairs = nt * (nt + 1) / 2;
+  const int s = local / pairs;
+  int p = local - s * pairs;
+  int ti = 0;
+  while (p >= nt - ti) {
+    p -= nt - ti;
+    ++ti;
+  }
+  const int tj = ti + p;
+  const int kbeg = s * ci.klen;
+  const int kend = min(rows, kbeg + ci.klen);
+  const bool full = VEC && (tj + 1) * BG <= d.r && (kend - kbeg) % BK == 0;
+  if (full) gram_body<BG, VEC, true>(L, d, Q, s, ti, tj, kbeg, kend, smem);
+  else gram_body<BG, VEC, false>(L, d, Q, s, ti, tj, kbeg, kend, smem);
+}
+
+// Four blocks per CU (at most 128 registers per lane): the float64 MFMAs
+// are long, and the extra wavefronts cover the tile loads and barriers.
 template <int BG, bool VEC>
 __global__ __launch_bounds__(kThreads, 4) void k_gram(Launch L) {
   constexpr int BK = 32;
   __shared__ f32x4 smem[mainloop_cells<BG, BG, BK>()];
-  for (int t = blockIdx.x; t < L.total; t += gridDim.x) {
-    MatDesc d;
-    ClassInfo ci;
-    int local;
-    locate(L, gridDim.x == L.total ? xcd_remap(t, gridDim.x) : t, d, ci, local);
-    if (skipped(L, d)) continue;
-    const int rows = L.which == 0 ? d.m : d.n;
-    const int nt = ci.tx;
-    const int pairs = nt * (nt + 1) / 2;
-    const int s = local / pairs;
-    int p = local - s * pairs;
-    int ti = 0;
-    while (p >= nt - ti) {
-      p -= nt - ti;
-      ++ti;
-    }
-    const int tj = ti + p;
-    const int kbeg = s * ci.klen;
-    const int kend = min(rows, kbeg + ci.klen);
-    const bool full = VEC && (tj + 1) * BG <= d.r && (kend - kbeg) % BK == 0;
-    if (full) gram_body<BG, VEC, true>(L, d, s, ti, tj, kbeg, kend, smem);
-    else gram_body<BG, VEC, false>(L, d, s, ti, tj, kbeg, kend, smem);
+  MatDesc d;
+  ClassInfo ci;
+  int local;
+  locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
+  if (skipped(L, d)) return;
+  gram_item<BG, VEC>(L, d, first_src(L, d), ci, local, smem);
+}
+
+// The same for the gated launches of orth's extra passes (see
+// dion_types.h): fewer workgroups than items, each taking a chunk
+// (for_items).
+template <int BG, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_gram_gated(Launch L) {
+  constexpr int BK = 32;
+  __shared__ f32x4 smem[mainloop_cells<BG, BG, BK>()];
+  for_items(L, [&](const MatDesc& d, const ClassInfo& ci, int local) {
+    gram_item<BG, VEC>(L, d, orth_src(L, d), ci, local, smem);
     __syncthreads();   // the next item reuses the LDS stages
-  }
+  });
 }
 
 // Q' = Q T^{-1}.  T^{-1} is upper triangular, so output column block tn
@@ -329,8 +346,8 @@ template <int BN, bool VEC, bool FULL>
 __device__ __forceinline__ void trmm_body(const Launch& L, const MatDesc& d, int rows, int tm,
                                           int tn, int kend, f32x4* smem) {
   constexpr int BK = 32;
-  const float* Q = orth_src(L, d);
-  float* dst = orth_dst(L, d);
+  const float* Q = first_src(L, d);
+  float* dst = final_dst(L, d);
   const double* Y = reinterpret_cast<const double*>(L.ws + d.oY);
   LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{Q}, d.r, tm * BM, rows, kend);
   LoadKC<BN, BK, true, true, SrcF64> lb(SrcF64{Y}, d.rp, tn * BN, d.r, kend);
@@ -349,12 +366,6 @@ __global__ __launch_bounds__(kThreads) void k_trmm(Launch L) {
   int local;
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
-  // matrices that take a second pass do this product in float64 later
-  const int32_t more = orth_decision(L, d);
-  if (more) {
-    if (local == 0 && threadIdx.x == 0) atomicOr(&L.status[d.slot], more);
-    return;
-  }
   const int rows = L.which == 0 ? d.m : d.n;
   int tm, tn;
   tile_order(local, ci.tx, ci.ty, tm, tn);
@@ -375,8 +386,8 @@ __device__ __forceinline__ void trmm6_body(const Launch& L, const MatDesc& d, in
   constexpr int BK = 16;
   constexpr int CA = BfShape<BM, BK>::CELLS, CB = BfShape<BN, BK>::CELLS;
   constexpr int STAGE = 3 * (CA + CB);
-  const float* Q = orth_src(L, d);
-  float* dst = orth_dst(L, d);
+  const float* Q = first_src(L, d);
+  float* dst = final_dst(L, d);
   const double* Y = reinterpret_cast<const double*>(L.ws + d.oY);
   LoadKC<BM, BK, VEC, false, SrcF32> la(SrcF32{Q}, d.r, tm * BM, rows, kend);
   LoadKC<BN, BK, true, true, SrcF64> lb(SrcF64{Y}, d.rp, tn * BN, d.r, kend);
@@ -416,12 +427,6 @@ __global__ __launch_bounds__(kThreads, 3) void k_trmm6(Launch L) {
   int local;
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
-  // matrices that take a second pass do this product in float64 later
-  const int32_t more = orth_decision(L, d);
-  if (more) {
-    if (local == 0 && threadIdx.x == 0) atomicOr(&L.status[d.slot], more);
-    return;
-  }
   const int rows = L.which == 0 ? d.m : d.n;
   int tm, tn;
   tile_order(local, ci.tx, ci.ty, tm, tn);
@@ -942,10 +947,13 @@ hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, int math, h
 }
 
 hipError_t launch_gram(const Launch& L, int bg, bool vec, hipStream_t st) {
-  // gated launches (only some matrices need them) run a capped grid
-  const int g = L.gate >= kGateRetry ? gated_grid(L.total) : L.total;
-  if (bg == 128) return vec ? go(k_gram<128, true>, L, st, kThreads, g) : go(k_gram<128, false>, L, st, kThreads, g);
-  return vec ? go(k_gram<64, true>, L, st, kThreads, g) : go(k_gram<64, false>, L, st, kThreads, g);
+  if (L.gate >= kGateRetry) {   // gated (only some matrices need it): a capped grid
+    const int g = gated_grid(L.total);
+    return vec ? go(k_gram_gated<64, true>, L, st, kThreads, g)
+               : go(k_gram_gated<64, false>, L, st, kThreads, g);
+  }
+  if (bg == 128) return vec ? go(k_gram<128, true>, L, st) : go(k_gram<128, false>, L, st);
+  return vec ? go(k_gram<64, true>, L, st) : go(k_gram<64, false>, L, st);
 }
 
 hipError_t launch_trmm(const Launch& L, int bn, bool vec, int math, hipStream_t st) {

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void k_qmax(Launch L) {
   const int rows = L.which == 0 ? d.m : d.n;
   const int groups = (d.r + 255) / 256;
   const int sp = local / groups, cg = local - sp * groups;
-  gptr<const uint32_t> Q = to_global(reinterpret_cast<const uint32_t*>(orth_src(L, d)));
+  gptr<const uint32_t> Q = to_global(reinterpret_cast<const uint32_t*>(first_src(L, d)));
   const int lane = threadIdx.x & 63, rg = threadIdx.x >> 6;
   int cc[4];
 #pragma unroll
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void k_qslice(Launch L) {
   if (!bad && mx != 0) frexpf(__uint_as_float(mx), &e);   // max |q| < 2^e
   if (kb == 0 && h == 0)
     reinterpret_cast<int*>(L.ws + d.oQ + q_exp_off(rmax, d.r))[col] = bad ? kQBadExp : e;
-  gptr<const float> Q = to_global(orth_src(L, d));
+  gptr<const float> Q = to_global(first_src(L, d));
   uint32_t w[kQDigits][4];
 #pragma unroll
   for (int t = 0; t < kQDigits; ++t)

@@ -29,6 +29,9 @@ hipError_t launch_chol_trail(const Launch& L, hipStream_t st);
 // the whole factorization of each matrix in one workgroup (shifted retry,
 // second pass) and the float64 triangular multiply that follows it
 hipError_t launch_chol_one(const Launch& L, hipStream_t st);
+// sets the per-matrix decision whether orth takes more passes (one
+// workgroup per matrix, after the first pass's factorization)
+hipError_t launch_orth_decide(const Launch& L, hipStream_t st);
 hipError_t launch_trmm64(const Launch& L, hipStream_t st);
 
 hipError_t launch_reduce(const Launch& L, hipStream_t st);

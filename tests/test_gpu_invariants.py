@@ -9,7 +9,8 @@ boundaries.
 * Orth-Dion: every nonzero singular value of ΔX is η (the dual-norm factor
   is one).  Dion: η ≤ ‖ΔX‖₂ ≤ η √r.
 * Uᵀ R_new = 0: the new residual has no component in span(U).  U is
-  recovered from the outputs as U = −ΔX V̄ (V̄ᵀV̄)⁻¹ / η.
+  recovered from the outputs as U = −ΔX V̄ (V̄ᵀV̄)⁻¹ / η (the oracle's
+  checks.left_factor_from_update).
 """
 import math
 
@@ -17,6 +18,7 @@ import numpy as np
 import pytest
 
 from oracle import DION, ORTH
+from oracle.checks import left_factor_from_update
 from workloads.configs import MatrixSpec, Workload
 
 from .gpuhelp import Case, f32, say
@@ -62,7 +64,7 @@ def test_update_invariants(gpu_lib, m, n, r, variant, arith):
     else:
         assert eta * (1 - 1e-4) <= sv[0] <= eta * math.sqrt(r) * (1 + 1e-4)
 
-    u = -(dx @ vb @ np.linalg.inv(gram)) / eta
+    u = left_factor_from_update(x0, x0 + dx, vb, eta)
     assert np.abs(u.T @ u - np.eye(r)).max() < 1e-4
     # residual orthogonal to span(U), relative to the residual's own size
     assert np.linalg.norm(u.T @ r_new) < 1e-4 * np.linalg.norm(r_new)
