@@ -199,6 +199,24 @@ int dion_step(float* X, const void* G, float* R, float* V,
               int variant, int g_dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* dion_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops or harnesses that forbid allocation): the
+ * same step with the same kernels, its workspace taken from a scratch array
+ * that the library holds on each GPU (32 MiB, kept until the process ends)
+ * instead of a caller buffer.  No device memory is allocated or freed.
+ * Shapes whose workspace (dion_workspace_size) exceeds 32 MiB are rejected
+ * with DION_ERR_WORKSPACE before any HIP call (for example 1024 x 1024 at
+ * rank 256, or 768 x 3072 at rank 192, fit; 2048 x 2048 at rank 512 does
+ * not).  All calls on one GPU share its scratch, so calls that overlap on
+ * one GPU (other streams, other threads) race; calls in stream order do
+ * not.  status_out (optional, a device pointer to one int) receives the
+ * matrix's status word when the step ends: its bits 0-7 are the
+ * DION_STATUS_* flags (0: the step was applied); higher bits are internal.
+ * Other arguments and errors as dion_step. */
+int dion_step_noalloc(float* X, const void* G, float* R, float* V,
+                      int64_t m, int64_t n, int64_t r, float eta, float beta,
+                      int variant, int g_dtype, int* status_out, void* stream);
+
 /* Grouped step: the same update applied to each matrix of a list (for
  * example all weight matrices of a model) with a handful of kernel launches
  * for the whole list.  The pages apply the step to every weight matrix

@@ -18,8 +18,8 @@ from typing import List, Optional, Sequence, Tuple
 
 __all__ = [
     "DionError", "Breakdown", "Plan", "load", "library_path", "workspace_size",
-    "workspace_size_batched", "step", "step_batched", "status", "check_status",
-    "version", "VARIANTS",
+    "workspace_size_batched", "step", "step_batched", "step_noalloc", "status",
+    "check_status", "version", "VARIANTS",
 ]
 
 OK = 0
@@ -100,6 +100,8 @@ def load() -> ctypes.CDLL:
                                            ctypes.POINTER(c_size)]),
         "dion_plan_buffer": (c_int, [vp, c_int, c_int, ctypes.POINTER(c_size),
                                      ctypes.POINTER(c_size)]),
+        "dion_step_noalloc": (c_int, [vp, vp, vp, vp, c_i64, c_i64, c_i64, c_f, c_f, c_int,
+                                      c_int, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -209,6 +211,24 @@ def step(X, G, R, V, eta: float, beta: float, variant="orth", workspace=None, st
     if rc != OK:
         raise _err(rc)
     return ws
+
+
+def step_noalloc(X, G, R, V, eta: float, beta: float, variant="orth", status_out=None,
+                 stream=None, math="f32"):
+    """One step on one matrix with the library's own scratch (no workspace
+    argument; dion_step_noalloc).  status_out: optional int32 GPU tensor of
+    one element that receives the matrix's status word."""
+    m, n, r = _check(X, G, R, V)
+    lib = load()
+    if status_out is not None and (not status_out.is_cuda or status_out.numel() < 1 or
+                                   status_out.dtype != _torch().int32):
+        raise ValueError("status_out must be an int32 GPU tensor")
+    rc = lib.dion_step_noalloc(X.data_ptr(), G.data_ptr(), R.data_ptr(), V.data_ptr(), m, n, r,
+                               float(eta), float(beta), _variant(variant, math), _gdtype(G),
+                               status_out.data_ptr() if status_out is not None else None,
+                               _stream_handle(stream, X.device))
+    if rc != OK:
+        raise _err(rc)
 
 
 def _mat_array(mats: Sequence[Tuple]) -> Tuple[ctypes.Array, int]:

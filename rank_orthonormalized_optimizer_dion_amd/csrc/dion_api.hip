@@ -751,6 +751,30 @@ std::vector<uint64_t> make_key(const dion_matrix* mats, int count, int variant, 
   return k;
 }
 
+// Scratch of dion_step_noalloc: the step's workspace in a file-scope device
+// array, for callers that cannot allocate device memory.  Each GPU the
+// library runs on holds its own copy until the process ends; its address on
+// a device is taken once, with that device current, and kept per device.
+// Calls on one GPU share it, so calls that overlap there race.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DION_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DION_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DION_OK;
+}
+
 }  // namespace
 }  // namespace dion
 
@@ -797,6 +821,27 @@ DION_API int dion_step(float* X, const void* G, float* R, float* V, int64_t m, i
   const hipError_t e = run_step(p, nullptr, eta, beta, static_cast<char*>(workspace),
                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DION_OK : DION_ERR_HIP;
+}
+
+DION_API int dion_step_noalloc(float* X, const void* G, float* R, float* V, int64_t m,
+                               int64_t n, int64_t r, float eta, float beta, int variant,
+                               int g_dtype, int* status_out, void* stream) {
+  dion_matrix a{X, G, R, V, m, n, r};
+  dion_plan p;
+  int rc = build_plan(&a, 1, variant, g_dtype, true, p);
+  if (rc != DION_OK) return rc;
+  if (!std::isfinite(eta) || !std::isfinite(beta)) return DION_ERR_INVALID_ARG;
+  if (p.ws_bytes > kScratchBytes) return DION_ERR_WORKSPACE;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != DION_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (run_step(p, nullptr, eta, beta, static_cast<char*>(ws), st) != hipSuccess) return DION_ERR_HIP;
+  if (status_out &&
+      hipMemcpyAsync(status_out, static_cast<char*>(ws) + p.status_off, sizeof(int32_t),
+                     hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return DION_ERR_HIP;
+  return DION_OK;
 }
 
 DION_API size_t dion_workspace_size_batched(const dion_matrix* mats, int count, int variant,
