@@ -111,6 +111,16 @@ extern "C" {
  *   cores (products exact, float64 rounding only). */
 #define DION_GRAM_F64     0x400
 
+/* Schedule of small matrices.  By default a matrix with r <= 16 whose
+ * step is small (factors P, W and V within 64 KB once their columns are
+ * padded to 8 or 16, and m n r <= 2^21) takes the whole step in one
+ * workgroup of one launch: float32 products, float64 Gram matrix and
+ * Cholesky, float64 triangular products (the math mode does not apply to
+ * it).  DION_SCHED_GROUPED, OR-ed into `variant`, sends every matrix
+ * through the grouped multi-launch schedule instead.  Sharded plans always
+ * use the grouped schedule. */
+#define DION_SCHED_GROUPED 0x800
+
 /* Row-sharded step (FSDP layout; the sharded setting the Dion and
  * Orth-Dion abstracts motivate).  OR DION_SHARDED into the variant of
  * dion_plan_create for a plan whose matrices are the local row shards of

@@ -32,6 +32,7 @@ VARIANTS = {"dion": 0, "orth": 1}
 MATH = {"f32": 0x000, "bf16x3": 0x100}
 SHARDED = 0x200
 GRAM_F64 = 0x400   # OR into math: float64 MFMA Gram matrix instead of sliced int8
+SCHED_GROUPED = 0x800   # OR into math: small matrices through the grouped schedule too
 SHARD_GRAM, SHARD_W = 0, 1
 BUF_W, BUF_P, BUF_U = 1, 2, 3   # dion_plan_buffer: intermediate factors of the last step
 STATUS_ORTH_P, STATUS_ORTH_W, STATUS_COLNORM = 1, 2, 4

@@ -64,7 +64,25 @@ struct ClassRec {
   int s_mv, kl_mv, s_mtu, kl_mtu, s_gp, kl_gp, s_gw, kl_gw;
   int s_cn, kl_cn;  // Dion column norms: row slices (<= 64, so the slices'
                     // float64 sums fit the Gram area, rp^2 >= 64 r) and rows per slice
+  int small_rb;     // > 0: the whole step in one workgroup (k_small), with
+                    // this rank block; such classes take no grouped launch
+  bool small_res;   // k_small with M resident in LDS
 };
+
+// Whether a matrix takes the one-workgroup step (k_small): r <= 16, its
+// factors fit that kernel's LDS, and each of its four products is at most
+// 2^21 multiply-adds (about 15 us of one compute unit's float32 FMAs).
+// Returns the rank block, or 0; resident: M fits in LDS as well.
+int small_block(int64_t m, int64_t n, int64_t r, bool& resident) {
+  resident = false;
+  const int rb = small_rank_block(static_cast<int>(r));
+  if (rb == 0) return 0;
+  const int64_t n32 = (n + 31) / 32 * 32;
+  if ((m + n + n32) * rb > kSmallFactorFloats) return 0;
+  if (m * n * r > (int64_t{1} << 21)) return 0;
+  resident = m * (n + 1) + (m + n32) * (rb + 1) <= kSmallResidentFloats;
+  return rb;
+}
 
 }  // namespace
 }  // namespace dion
@@ -139,7 +157,8 @@ void pick_split(int64_t tiles, int K, int& s, int& klen) {
 int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool single,
                dion_plan& p) {
   if (!mats || count < 1) return DION_ERR_INVALID_ARG;
-  if (variant & ~(DION_VARIANT_MASK | DION_MATH_MASK | DION_SHARDED | DION_GRAM_F64))
+  if (variant & ~(DION_VARIANT_MASK | DION_MATH_MASK | DION_SHARDED | DION_GRAM_F64 |
+                  DION_SCHED_GROUPED))
     return DION_ERR_INVALID_ARG;
   if ((variant & DION_SHARDED) && single) return DION_ERR_INVALID_ARG;
   const int rule = variant & DION_VARIANT_MASK;
@@ -184,6 +203,8 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
       const bool big_r = k.r * 10 >= cdiv(k.r, 256) * 256 * 9;   // <= 10% of 256-wide tiles idle
       k.bn_mv = p.math && k.m >= 256 && big_r ? 256 : k.bn_r;
       k.bn_mtu = p.math && k.n >= 256 && big_r ? 256 : k.bn_r;
+      k.small_rb = p.sharded || (variant & DION_SCHED_GROUPED)
+                       ? 0 : small_block(k.m, k.n, k.r, k.small_res);
       p.cls.push_back(k);
     }
     cls_of[i] = c;
@@ -281,10 +302,13 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
 // Classes with the longest reduction per work item go first (longest job
 // first), so that a launch does not end on a last round of its slowest
 // blocks; classes of equal length keep their order.
+// Classes of the one-workgroup step (small_rb > 0) take part only when
+// `small` is set, and then alone.
 template <class Fill, class Go>
-hipError_t grouped(const dion_plan& p, const Launch& base, Fill fill, Go go) {
+hipError_t grouped(const dion_plan& p, const Launch& base, Fill fill, Go go, bool small = false) {
   std::vector<ClassInfo> todo;
   for (const ClassRec& c : p.cls) {
+    if ((c.small_rb > 0) != small) continue;
     ClassInfo ci{};
     if (!fill(c, ci) || ci.tiles <= 0) continue;
     ci.first = c.first;
@@ -535,9 +559,20 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   const int ept = elems_per_tile();
 
   if (first <= 0 && last >= 0) {
+  DION_TRY(mk.mark(0, st));
+  // small matrices: the whole step in one workgroup each
+  for (int rb : {8, 16})
+    for (bool res : {true, false}) {
+      Launch sl = base;
+      sl.mode = p.variant == DION_VARIANT_ORTH ? 1 : 0;
+      DION_TRY(grouped(p, sl, [&](const ClassRec& c, ClassInfo& ci) {
+        if (c.small_rb != rb || c.small_res != res) return false;
+        ci.tiles = 1;
+        return true;
+      }, [&](const Launch& L) { return launch_small(L, p.gdtype, rb, res, st); }, true));
+    }
   // P = M V (split-bfloat16: V^T split once into planes, read as whole cells
   // by every tile)
-  DION_TRY(mk.mark(0, st));
   if (p.math) DION_TRY(split_t(p, base, 0, st));
   for (int bn : {256, 128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {

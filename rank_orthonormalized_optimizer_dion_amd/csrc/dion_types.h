@@ -10,6 +10,16 @@ constexpr int kCholNB = 64;
 // columns (the reduction tile of the kernels that read them).
 constexpr int kPlaneK = 32;
 inline __host__ __device__ int plane_pitch(int rows) { return (rows + kPlaneK - 1) / kPlaneK * kPlaneK; }
+// The one-workgroup step of a small matrix (k_small): r <= kSmallMaxRank,
+// and the factors P / U, W and V / Vbar, columns padded to rb (8 or 16) and
+// V's rows to a multiple of 32, in kSmallFactorFloats float32 values of
+// LDS: (m + n + n32) rb <= kSmallFactorFloats.
+constexpr int kSmallMaxRank = 16;
+constexpr int kSmallFactorFloats = 16384;
+// Its resident form keeps M = G + R in LDS as well, read from global memory
+// once, and pads the factors' rows to rb + 1: m (n + 1) + (m + n32) (rb + 1)
+// <= kSmallResidentFloats.
+constexpr int kSmallResidentFloats = 39680;
 // Grouped launches carry at most this many shape classes.
 constexpr int kMaxClasses = 8;
 

@@ -34,6 +34,13 @@ hipError_t launch_chol_one(const Launch& L, hipStream_t st);
 hipError_t launch_orth_decide(const Launch& L, hipStream_t st);
 hipError_t launch_trmm64(const Launch& L, hipStream_t st);
 
+// The whole step of each matrix of the launch in one workgroup (small
+// matrices; L.mode = 1 for Orth-Dion, 0 for Dion).  rb: the rank block
+// small_rank_block(r) of every matrix of the launch; resident: M is held in
+// LDS (every matrix of the launch fits kSmallResidentFloats).
+int small_rank_block(int r);   // 8, 16, or 0 when r > kSmallMaxRank
+hipError_t launch_small(const Launch& L, int gdtype, int rb, bool resident, hipStream_t st);
+
 hipError_t launch_reduce(const Launch& L, hipStream_t st);
 hipError_t launch_colnorm(const Launch& L, hipStream_t st);
 hipError_t launch_colnorm_fin(const Launch& L, hipStream_t st);

@@ -141,7 +141,15 @@ def test_gram_variant_bit(lib):
     f64 = lib.dion_workspace_size(m, n, r, 1 | dion.GRAM_F64, 1)
     assert f64 > 0
     assert sliced - f64 >= 5 * r * max(m, n)
-    assert lib.dion_workspace_size(m, n, r, 1 | 0x800, 1) == 0
+    assert lib.dion_workspace_size(m, n, r, 1 | 0x1000, 1) == 0
+
+
+def test_grouped_schedule_bit(lib):
+    # DION_SCHED_GROUPED is accepted and changes no workspace size
+    for m, n, r in ((256, 128, 16), (3072, 8192, 768)):
+        plain = lib.dion_workspace_size(m, n, r, 1, 0)
+        assert plain > 0
+        assert lib.dion_workspace_size(m, n, r, 1 | dion.SCHED_GROUPED, 0) == plain
 
 
 def test_binding_constants_match_header():
@@ -155,6 +163,7 @@ def test_binding_constants_match_header():
     assert defs["DION_MATH_BF16X3"] == dion.MATH["bf16x3"]
     assert defs["DION_GRAM_F64"] == dion.GRAM_F64
     assert defs["DION_SHARDED"] == dion.SHARDED
+    assert defs["DION_SCHED_GROUPED"] == dion.SCHED_GROUPED
     assert defs["DION_SHARD_GRAM"] == dion.SHARD_GRAM and defs["DION_SHARD_W"] == dion.SHARD_W
     assert (defs["DION_BUF_P"], defs["DION_BUF_U"], defs["DION_BUF_W"]) == \
         (dion.BUF_P, dion.BUF_U, dion.BUF_W)

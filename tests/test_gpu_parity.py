@@ -61,11 +61,14 @@ SHAPES = [
 @pytest.mark.parametrize("g_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("arith", ["f32", "bf16x3"])
 def test_ragged_shapes(gpu_lib, m, n, r, variant, g_dtype, arith):
+    # the grouped schedule's kernels on every shape (small ones included:
+    # their own one-workgroup step is tested in test_gpu_small.py)
     wl = _wl(m, n, r, g_dtype)
     c = Case(wl, wl.mats[0])
     c.load_grad(0)
     say(f"ragged {m}x{n} r={r} {variant} {g_dtype} {arith}")
-    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant, math=arith)
+    gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, variant,
+                 math=gpu_lib.MATH[arith] | gpu_lib.SCHED_GROUPED)
     res, x_prev = c.oracle(variant)
     assert_close(c.errors(x_prev, res.M), TOL_1, f"{m}x{n} r={r} {variant} {g_dtype}")
 
