@@ -124,26 +124,30 @@ def make_stack(wl, device):
     return out
 
 
-def time_plan(dion, torch, mats, variant, steps, warmup, eta, beta, math="f32"):
+def time_plan(dion, torch, mats, variant, steps, warmup, eta, beta, math="f32", phases=True):
+    """Seconds per step over `steps` timed steps, and the per-phase HIP-event
+    times of those same steps (phases=False: no phase events, for steps so
+    short that recording them would be a visible part of the step)."""
     plan = dion.Plan([(d.X, d.G, d.R, d.V) for d in mats], variant, math=math)
     ws = plan.new_workspace()
     for _ in range(warmup):
         plan.step(eta, beta, ws)
     torch.cuda.synchronize()
-    plan.timing_enable(steps)
+    if phases:
+        plan.timing_enable(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         plan.step(eta, beta, ws)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    phases, n = plan.timing_read()
+    ph, n = plan.timing_read() if phases else ({}, 1)
     rc, per = dion.status(ws, plan.count)
     plan.close()
     del ws
     if rc != 0:
         raise RuntimeError(f"breakdown during the benchmark: {per}")
-    return (t1 - t0) / steps, {k: v / n for k, v in phases.items()}
+    return (t1 - t0) / steps, {k: v / n for k, v in ph.items()}
 
 
 def time_sharded(dion, torch, whole, shards, variant, steps, warmup, eta, beta, math):
@@ -302,7 +306,7 @@ def step_roofline_entry(shapes, variant: str, eg: int, math: str, sec: float) ->
 
 # the other workloads: (label, config number, rank for config 5, timed steps,
 # oracle sample: (matrix indices, steps), single-threaded oracle too)
-OTHER_CONFIGS = (("single-256x128", 1, None, 200, ((0,), 10), True),
+OTHER_CONFIGS = (("single-256x128", 1, None, 1000, ((0,), 10), True),
                  ("planted-2048", 2, None, 40, ((0,), 3), True),
                  ("gpt160m-stack", 3, None, 30, (tuple(range(72)), 1), False),
                  ("mlp70b-r512", 5, 512, 10, ((0,), 1), False),
@@ -326,7 +330,8 @@ def time_configs(dion, torch, dev, math: str, cpu: bool = True):
         shapes = [(s.m, s.n, s.r) for s in wl.mats]
         eg = 2 if wl.g_dtype == "bf16" else 4
         for var in ("orth", "dion"):
-            sec, _ = time_plan(dion, torch, mats, var, steps, 3, wl.eta, wl.beta, math)
+            sec, _ = time_plan(dion, torch, mats, var, steps, 3, wl.eta, wl.beta, math,
+                               phases=False)
             entry = {"workload": wl.name, "steps_per_s": round(1 / sec, 2),
                      "ms_per_step": round(sec * 1e3, 4),
                      "step_roofline": step_roofline_entry(shapes, var, eg, math, sec)}

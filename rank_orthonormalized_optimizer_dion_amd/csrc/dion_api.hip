@@ -161,6 +161,9 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
                   DION_SCHED_GROUPED))
     return DION_ERR_INVALID_ARG;
   if ((variant & DION_SHARDED) && single) return DION_ERR_INVALID_ARG;
+  // one matrix: its descriptor travels in the kernel arguments (no table in
+  // the workspace, nothing copied from the host per step)
+  single = single || count == 1;
   const int rule = variant & DION_VARIANT_MASK;
   if (rule != DION_VARIANT_DION && rule != DION_VARIANT_ORTH) return DION_ERR_INVALID_ARG;
   if (gdtype != DION_DTYPE_F32 && gdtype != DION_DTYPE_BF16) return DION_ERR_INVALID_ARG;
@@ -724,12 +727,15 @@ int plan_step(dion_plan* p, float eta, float beta, void* ws, size_t bytes, hipSt
   int rc = check_call(*p, eta, beta, ws, bytes);
   if (rc != DION_OK) return rc;
   char* w = static_cast<char*>(ws);
-  MatDesc* dev_table = reinterpret_cast<MatDesc*>(w + p->table_off);
-  if (hipMemcpyAsync(dev_table, p->pinned, sizeof(MatDesc) * p->count, hipMemcpyHostToDevice,
-                     st) != hipSuccess)
-    return DION_ERR_HIP;
-  if (hipEventRecord(p->ev, st) != hipSuccess) return DION_ERR_HIP;
-  p->ev_pending = true;
+  MatDesc* dev_table = nullptr;
+  if (!p->single) {
+    dev_table = reinterpret_cast<MatDesc*>(w + p->table_off);
+    if (hipMemcpyAsync(dev_table, p->pinned, sizeof(MatDesc) * p->count, hipMemcpyHostToDevice,
+                       st) != hipSuccess)
+      return DION_ERR_HIP;
+    if (hipEventRecord(p->ev, st) != hipSuccess) return DION_ERR_HIP;
+    p->ev_pending = true;
+  }
   Marker mk;
   if (first == 0 && last == 2 && p->t_count < p->t_max)
     mk.ev = &p->tev[static_cast<size_t>(p->t_count++) * (DION_PHASES + 1)];
