@@ -121,6 +121,10 @@ __device__ __forceinline__ float* orth_dst(const Launch& L, const MatDesc& d) {
 // the workgroup (it may contain barriers).
 template <class F>
 __device__ __forceinline__ void for_items(const Launch& L, F&& body) {
+  // no matrix of the factorization needs this gate: one load and done
+  const int32_t any = L.status[L.any_slot];
+  if ((L.gate == kGateRetry && !(any & kCtlRetry)) || (L.gate == kGateTwo && !(any & kCtlTwo)))
+    return;
   if (static_cast<int>(gridDim.x) >= L.total) {
     MatDesc d;
     ClassInfo ci;

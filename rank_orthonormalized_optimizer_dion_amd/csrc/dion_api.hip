@@ -242,10 +242,12 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     k.kl_cn = cdiv(k.n, k.s_cn);
     k.s_cn = cdiv(k.n, k.kl_cn);
   }
-  // Workspace: status words | matrix table (grouped calls) | per-matrix buffers.
+  // Workspace: status words (one per matrix, then the union of the control
+  // bits of the factorization in progress) | matrix table (grouped calls) |
+  // per-matrix buffers.
   size_t off = 0;
   p.status_off = off;
-  off = align_up(off + static_cast<size_t>(count) * 4);
+  off = align_up(off + static_cast<size_t>(count + 1) * 4);
   p.table_off = off;
   if (!single) off = align_up(off + static_cast<size_t>(count) * sizeof(MatDesc));
   p.table.resize(count);
@@ -457,7 +459,7 @@ hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
   DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
     const int nb = c.rp / kCholNB;
     ci.splits = which == 0 ? c.s_gp : c.s_gw;
-    ci.tiles = nb * (nb + 1) / 2;
+    ci.tiles = nb * (nb + 1) / 2 * kCholInitParts;
     return true;
   }, [&](const Launch& L) { return launch_chol_init(L, st); }));
   // block steps in pairs (kb, kb + 1) with look-ahead: factor kb, bring
@@ -557,6 +559,7 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   if (p.single) base.inl = p.table[0];
   base.ws = ws;
   base.status = reinterpret_cast<int32_t*>(ws + p.status_off);
+  base.any_slot = p.count;
   base.eta = eta;
   base.beta = beta;
   const int ept = elems_per_tile();

@@ -146,6 +146,9 @@ struct Launch {
   int32_t gate;           // Gate: which matrices the launch works on
   int32_t retry;          // first pass: 1 = small pivots lead to a second pass or
                           // the shifted retry, 0 = they are breakdowns
+  int32_t any_slot;       // status[any_slot]: the control bits of every matrix of
+                          // the factorization in progress, OR-ed together (so
+                          // that a gated launch no matrix needs ends at once)
 };
 
 }  // namespace dion

@@ -88,50 +88,70 @@ __device__ __forceinline__ int64_t block_off(int fm, int fn, int v, int64_t ld) 
   return row * ld + col;
 }
 
+// A = the Gram matrix (the sum of its reduction slices' partials, upper
+// triangle, mirrored), rows past r padded with the identity; diag(S) kept
+// aside.  Work item: a quarter (16 rows) of one 64 x 64 upper block; each
+// thread takes 4 elements and issues all their partials' loads before
+// adding them (in slice order).
+constexpr int kInitParts = kCholInitParts;
 __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
   MatDesc d;
   ClassInfo ci;
   int local;
+  // A factorization starts with no control bits (no other kernel of this
+  // launch reads them), in the matrices' words and in their union
+  if (blockIdx.x == 0 && threadIdx.x == 0) L.status[L.any_slot] = 0;
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
-  // A factorization starts with no control bits (no other kernel of this
-  // launch reads them)
   if (local == 0 && threadIdx.x == 0) L.status[d.slot] &= kStatusMask;
+  const int quarter = local % kInitParts;
   const int nblk = d.rp / NB;
-  int p = local, bi = 0;
+  int p = local / kInitParts, bi = 0;
   while (p >= nblk - bi) {
     p -= nblk - bi;
     ++bi;
   }
   const int bj = bi + p;
-  const double* S = reinterpret_cast<const double*>(L.ws + d.oS);
+  gptr<const double> S = to_global(reinterpret_cast<const double*>(L.ws + d.oS));
   double* A = dptr(L, d.oA);
   double* Sd = dptr(L, d.oD) + NB * NB;
   const int64_t rp = d.rp, plane = rp * rp;
-  for (int e = threadIdx.x; e < NB * NB; e += kThreads) {
-    const int gi = bi * NB + e / NB, gj = bj * NB + e % NB;
-    double v;
-    if (gi < d.r && gj < d.r) {
-      // the Gram kernel writes the upper triangle (gi <= gj) only
-      const int64_t e = static_cast<int64_t>(min(gi, gj)) * rp + max(gi, gj);
-      v = 0.0;
-      for (int s = 0; s < ci.splits; ++s) v += S[s * plane + e];
-    } else {
-      v = gi == gj ? 1.0 : 0.0;
-    }
-    A[gi * rp + gj] = v;
-    if (gi == gj) Sd[gi] = v;
+  constexpr int ROWS = NB / kInitParts, PER = ROWS * NB / kThreads;
+  static_assert(PER * kThreads == ROWS * NB, "whole elements per thread");
+  int gi[PER], gj[PER];
+  int64_t e[PER];
+  bool in[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int el = threadIdx.x + kThreads * u;
+    gi[u] = bi * NB + quarter * ROWS + el / NB;
+    gj[u] = bj * NB + el % NB;
+    in[u] = gi[u] < d.r && gj[u] < d.r;
+    // the Gram kernels write the upper triangle (gi <= gj) only
+    e[u] = static_cast<int64_t>(min(gi[u], gj[u])) * rp + max(gi[u], gj[u]);
+  }
+  double acc[PER] = {};
+  constexpr int kSlices = 8;   // slices' loads in flight per element
+  for (int s0 = 0; s0 < ci.splits; s0 += kSlices) {
+    double v[kSlices][PER];
+#pragma unroll
+    for (int q = 0; q < kSlices; ++q)
+#pragma unroll
+      for (int u = 0; u < PER; ++u)
+        v[q][u] = in[u] && s0 + q < ci.splits ? S[(s0 + q) * plane + e[u]] : 0.0;
+#pragma unroll
+    for (int q = 0; q < kSlices; ++q)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] += v[q][u];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const double val = in[u] ? acc[u] : (gi[u] == gj[u] ? 1.0 : 0.0);
+    A[gi[u] * rp + gj[u]] = val;
+    if (gi[u] == gj[u]) Sd[gi[u]] = val;
   }
 }
 
-// One 64 x 64 diagonal block: T_kk (upper, positive diagonal) with
-// T_kk^T T_kk = A_kk, and Z = T_kk^{-T} from the same row operations on an
-// identity block.  Thread (wavefront w, lane c) keeps rows 4 q + w of column
-// c of both in registers; step k's scaled pivot row is broadcast through a
-// double-buffered LDS row, so one barrier per step suffices (a buffer is
-// rewritten two steps later, after every thread has passed the barrier that
-// follows its last read).  A failed pivot is flagged in the same buffer, so
-// every wavefront leaves the loop at the same step.
 // Sum of one value per thread over the workgroup, in a fixed order (lanes
 // by a butterfly, then the four wavefronts in turn), the same in every
 // thread.
@@ -145,85 +165,195 @@ __device__ __forceinline__ double block_sum(double v) {
   return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
+// One 64 x 64 diagonal block: T_kk (upper, positive diagonal) with
+// T_kk^T T_kk = A_kk, and Z = T_kk^{-T} from the same row operations on an
+// identity block, in eight steps of eight columns on the 16 x 16 x 4
+// float64 MFMA.  The block is 4 x 4 tiles of 16 x 16; wavefront w keeps
+// tile column w of A (tiles (I, w), I <= w: the upper triangle, the only
+// part read) and of Z (tiles (I, w), I >= w), each as an MFMA accumulator
+// (register v of lane 16 g + c: row 4 v + g, column c of the tile).
+// Step s (rows and columns 8 s .. 8 s + 7: registers 2 (s % 2) and
+// 2 (s % 2) + 1 of tile row s / 2):
+//   1. every lane factors the step's 8 x 8 diagonal block (from LDS) with
+//      the same float64 operations, checks its pivots and forms
+//      zt = t^{-T}, so every wavefront takes the same decisions without
+//      communicating;
+//   2. the step's rows of A and of Z become zt times themselves (two MFMAs
+//      per tile, the 16 x 4 operand holding zt): its rows of T, and of Z,
+//      are then final;
+//   3. the rows below take the rank-8 update A_IJ -= T_sI^T T_sJ and
+//      Z_IJ -= T_sI^T Z_sJ (T_s is exchanged through LDS; a tile that holds
+//      the step's own rows keeps them), the next step's 8 x 8 block first.
+// Every pivot is the Schur complement's diagonal, as in the column-by-column
+// factorization.
+constexpr int kRowPitch = NB + 16;   // LDS row pitch (doubles) of the step's T rows
+
+__device__ __forceinline__ f64x4 mfma64(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
 // Factors diagonal block kb of matrix d (Dinv and Y_kk written to the
 // workspace).  A pivot fails when it is not above tol times the column's
 // original squared norm (or is not finite); returns false then, with
 // nothing written.  small: some pivot ratio was below kRatioTwo.
 __device__ __forceinline__ bool diag_block(const Launch& L, const MatDesc& d, int kb, double tol,
                                            bool& small, double* part) {
-  __shared__ double rowA[2][NB];
-  __shared__ double rowZ[2][NB];
-  __shared__ double sd[NB];
-  __shared__ int badf[2];
-  __shared__ int smallf;
+  __shared__ double blk[8][8];                 // the step's 8 x 8 block (upper)
+  __shared__ double sdl[NB];                   // diag(S) of the block's columns
+  __shared__ double rows[8][kRowPitch];        // the step's 8 rows of T
+  __shared__ double ztl[kThreads / 64][8][8];  // zt, one copy per wavefront
   const int64_t rp = d.rp, o = static_cast<int64_t>(kb) * NB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
   gptr<const double> A = to_global(dptr(L, d.oA) + o * rp + o);
-  double a[NB / 4], z[NB / 4];
+  f64x4 ta[4], tz[4];
 #pragma unroll
-  for (int q = 0; q < NB / 4; ++q) {
-    a[q] = A[(4 * q + wave) * rp + lane];
-    z[q] = 4 * q + wave == lane ? 1.0 : 0.0;
-  }
-  if (threadIdx.x < NB) sd[threadIdx.x] = dptr(L, d.oD)[NB * NB + o + threadIdx.x];
-  if (threadIdx.x == 0) smallf = 0;
-  __syncthreads();
-  bool bad = false;
+  for (int I = 0; I < 4; ++I)
 #pragma unroll
-  for (int q = 0; q < NB / 4; ++q) {
-#pragma nounroll
-    for (int w = 0; w < 4; ++w) {
-      const int k = 4 * q + w, buf = k & 1;
-      if (wave == w) {   // this wavefront holds row k
-        const double dk = read_lane(a[q], k);
-        const bool ok = dk > tol * sd[k] && dk < INFINITY;
-        const double inv = rsqrt_nr(dk), t = dk * inv;
-        a[q] = lane > k ? a[q] * inv : (lane == k ? t : 0.0);
-        z[q] = lane <= k ? z[q] * inv : 0.0;
-        rowA[buf][lane] = a[q];
-        rowZ[buf][lane] = z[q];
-        if (lane == 0) {
-          badf[buf] = ok ? 0 : 1;
-          if (!(dk >= kRatioTwo * sd[k])) smallf = 1;
-        }
-      }
-      __syncthreads();
-      // every read of the broadcast row is issued before the first use
-      const int flag = badf[buf];
-      const double rj = rowA[buf][lane], zj = rowZ[buf][lane];
-      double ai[NB / 4];
-#pragma unroll
-      for (int qq = q; qq < NB / 4; ++qq) ai[qq] = rowA[buf][4 * qq + wave];
-      if (flag) {
-        bad = true;
-        break;
-      }
-#pragma unroll
-      for (int qq = q; qq < NB / 4; ++qq) {
-        if (qq == q && wave <= w) continue;   // rows 4 qq + wave <= k
-        if (lane > k) a[qq] -= ai[qq] * rj;
-        z[qq] -= ai[qq] * zj;
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * I + 4 * v + g, col = 16 * w + c;
+      ta[I][v] = I <= w ? A[row * rp + col] : 0.0;
+      tz[I][v] = I >= w && row == col ? 1.0 : 0.0;
     }
-    if (bad) break;
+  if (threadIdx.x < NB) sdl[threadIdx.x] = dptr(L, d.oD)[NB * NB + o + threadIdx.x];
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = i + 1; j < 8; ++j) ztl[w][i][j] = 0.0;
   }
-  small = smallf != 0;
-  if (bad) return false;
+  // the 8 x 8 block of step s, from registers 2 (s % 2) + h of tile
+  // (s / 2, s / 2) (held by wavefront s / 2)
+  auto put_block = [&](const f64x4& t, int s) {
+    const int c0 = 8 * (s % 2), v0 = 2 * (s % 2);
+    if (c >= c0 && c < c0 + 8) {
+      blk[g][c - c0] = t[v0];
+      blk[4 + g][c - c0] = t[v0 + 1];
+    }
+  };
+  if (w == 0) put_block(ta[0], 0);
+  __syncthreads();
+  bool sm = false;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int S = s / 2, v0 = 2 * (s % 2);
+    // 1. t^T t = the 8 x 8 block: f holds t above the diagonal and
+    // zt = t^{-T} on and below it
+    double f[8][8], sk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sk[i] = sdl[8 * s + i];
+#pragma unroll
+      for (int j = i; j < 8; ++j) f[i][j] = blk[i][j];
+    }
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const double dk = f[k][k];
+      ok = ok && dk > tol * sk[k] && dk < INFINITY;
+      sm = sm || !(dk >= kRatioTwo * sk[k]);
+      const double inv = rsqrt_nr(dk);
+      f[k][k] = inv;
+#pragma unroll
+      for (int j = k + 1; j < 8; ++j) f[k][j] *= inv;
+#pragma unroll
+      for (int i = k + 1; i < 8; ++i)
+#pragma unroll
+        for (int j = i; j < 8; ++j) f[i][j] -= f[k][i] * f[k][j];
+    }
+    if (!ok) {
+      small = sm;
+      return false;   // the same in every thread
+    }
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < i; ++j) {
+        double acc = 0.0;
+#pragma unroll
+        for (int m = j; m < i; ++m) acc += f[m][i] * (m == j ? f[j][j] : f[m][j]);
+        f[i][j] = -f[i][i] * acc;
+      }
+    // the MFMA operand of zt: lane l holds zt[l % 16][4 h + l / 16]
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j) ztl[w][i][j] = f[i][j];
+    }
+    asm volatile("" ::: "memory");   // lane 0's writes precede the reads (in-order LDS)
+    const double z0 = c < 8 ? ztl[w][c][g] : 0.0;
+    const double z1 = c < 8 ? ztl[w][c][4 + g] : 0.0;
+    // 2. the step's rows of A (tile (S, w), w >= S) and of Z (w <= S)
+    const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
+    if (w >= S) {
+      f64x4 r = mfma64(z0, ta[S][v0], zero);
+      r = mfma64(z1, ta[S][v0 + 1], r);
+      double x0 = r[0], x1 = r[1];
+      if (w == S) {   // T is upper triangular: exact zeros left of the diagonal
+        if (c < 8 * (s % 2) + g) x0 = 0.0;
+        if (c < 8 * (s % 2) + 4 + g) x1 = 0.0;
+      }
+      ta[S][v0] = x0;
+      ta[S][v0 + 1] = x1;
+      rows[g][16 * w + c] = x0;
+      rows[4 + g][16 * w + c] = x1;
+    }
+    if (w <= S) {
+      f64x4 r = mfma64(z0, tz[S][v0], zero);
+      r = mfma64(z1, tz[S][v0 + 1], r);
+      tz[S][v0] = r[0];
+      tz[S][v0 + 1] = r[1];
+    }
+    __syncthreads();
+    if (s == 7) break;
+    // 3. rank-8 update of the rows below the step's: lane l's operand of
+    // T_sI is T[8 s + 4 h + l / 16][16 I + l % 16]
+    auto update = [&](f64x4& t, int I, const f64x4& bsrc) {
+      // (t and bsrc are the same tile when I == S: operands first)
+      const double a0 = -rows[g][16 * I + c], a1 = -rows[4 + g][16 * I + c];
+      const double b0 = bsrc[v0], b1 = bsrc[v0 + 1];
+      const double keep0 = t[v0], keep1 = t[v0 + 1];
+      t = mfma64(a0, b0, t);
+      t = mfma64(a1, b1, t);
+      if (I == S) {   // the step's own rows stay as they are
+        t[v0] = keep0;
+        t[v0 + 1] = keep1;
+      }
+    };
+    const int Sn = (s + 1) / 2;
+    if (w == Sn) {   // the next step's block first
+      update(ta[Sn], Sn, ta[S]);
+      put_block(ta[Sn], s + 1);
+    }
+#pragma unroll
+    for (int I = S; I < 4; ++I)
+      if (I <= w && !(w == Sn && I == Sn)) update(ta[I], I, ta[S]);
+    if (w <= S) {
+#pragma unroll
+      for (int I = S; I < 4; ++I) update(tz[I], I, tz[S]);
+    }
+    __syncthreads();
+  }
+  small = sm;
   // Dinv = T_kk^{-1} = Z^T (upper triangular), Y_kk = Z (lower, zeros above).
   gptr<double> Dinv = to_global(dptr(L, d.oD));
   gptr<double> Y = to_global(dptr(L, d.oY) + o * rp + o);
-  double acc = 0.0;
+  double q = 0.0;
 #pragma unroll
-  for (int q = 0; q < NB / 4; ++q) {
-    const int i = 4 * q + wave;
-    Dinv[lane * NB + i] = lane <= i ? z[q] : 0.0;
-    Y[i * rp + lane] = z[q];
-    acc += z[q] * z[q];
-  }
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * I + 4 * v + g, col = 16 * w + c;
+      const double z = I >= w ? tz[I][v] : 0.0;
+      Dinv[col * NB + row] = z;
+      Y[row * rp + col] = z;
+      q += z * z;
+    }
   if (part) {
     // this block's share of trace(C^{-1}): S_cc Y_jc^2 over its columns c < r
-    const double w = o + lane < d.r ? sd[lane] : 0.0;
-    const double t = block_sum(w * acc);
+    const int col = 16 * w + c;
+    const double wt = o + col < d.r ? sdl[col] : 0.0;
+    const double t = block_sum(wt * q);
     if (threadIdx.x == 0) *part = t;
   }
   return true;
@@ -249,8 +379,12 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
   const bool ok = diag_block(L, d, L.kb, L.retry ? kRatioRetry : kRatioTwo, small,
                              trace_part(L, d, L.kb, L.kb));
   if (threadIdx.x == 0) {
-    if (!ok) atomicOr(&L.status[d.slot], L.retry ? (kCtlRetry | kCtlTwo) : L.flag);
-    else if (small && L.retry) atomicOr(&L.status[d.slot], kCtlTwo);
+    const int32_t bits = !ok ? (L.retry ? (kCtlRetry | kCtlTwo) : L.flag)
+                             : (small && L.retry ? kCtlTwo : 0);
+    if (bits) {
+      atomicOr(&L.status[d.slot], bits);
+      if (bits & (kCtlRetry | kCtlTwo)) atomicOr(&L.status[L.any_slot], bits);
+    }
   }
 }
 
@@ -404,7 +538,10 @@ __global__ __launch_bounds__(kThreads) void k_orth_decide(Launch L) {
     int32_t more = 0;
     if (!(t <= kTraceRetry * d.r)) more = kCtlTwo | kCtlRetry;
     else if (!(t <= kTraceTwo * d.r)) more = kCtlTwo;
-    if (more) atomicOr(&L.status[d.slot], more);
+    if (more) {
+      atomicOr(&L.status[d.slot], more);
+      atomicOr(&L.status[L.any_slot], more);
+    }
   }
 }
 
