@@ -25,6 +25,8 @@
 //   k_trmm64    Q T^{-1} with float64 products, rounded once to float32
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launchers.h"
 #include "orth_rules.h"
@@ -167,196 +169,215 @@ __device__ __forceinline__ double block_sum(double v) {
 
 // One 64 x 64 diagonal block: T_kk (upper, positive diagonal) with
 // T_kk^T T_kk = A_kk, and Z = T_kk^{-T} from the same row operations on an
-// identity block, in eight steps of eight columns on the 16 x 16 x 4
-// float64 MFMA.  The block is 4 x 4 tiles of 16 x 16; wavefront w keeps
-// tile column w of A (tiles (I, w), I <= w: the upper triangle, the only
-// part read) and of Z (tiles (I, w), I >= w), each as an MFMA accumulator
+// identity block, by one wavefront that holds the whole block.  It factors
+// the column-scaled block A' = D A_kk D, D = diag(S)^{-1/2} over the
+// block's columns (S the Gram matrix before any update): then T' = T_kk D,
+// Z = Z' D, every pivot of A' is the pivot ratio the checks compare, at
+// most 1, and the in-place row update below (B + (zt - I) B) keeps float64
+// accuracy relative to its result whatever the data's scale.  4 x 4 tiles
+// of 16 x 16, the ten upper tiles of A (the only part read) and the ten
+// lower tiles of Z, each as a 16 x 16 x 4 float64 MFMA accumulator
 // (register v of lane 16 g + c: row 4 v + g, column c of the tile).
-// Step s (rows and columns 8 s .. 8 s + 7: registers 2 (s % 2) and
-// 2 (s % 2) + 1 of tile row s / 2):
-//   1. every lane factors the step's 8 x 8 diagonal block (from LDS) with
-//      the same float64 operations, checks its pivots and forms
-//      zt = t^{-T}, so every wavefront takes the same decisions without
-//      communicating;
-//   2. the step's rows of A and of Z become zt times themselves (two MFMAs
-//      per tile, the 16 x 4 operand holding zt): its rows of T, and of Z,
-//      are then final;
-//   3. the rows below take the rank-8 update A_IJ -= T_sI^T T_sJ and
-//      Z_IJ -= T_sI^T Z_sJ (T_s is exchanged through LDS; a tile that holds
-//      the step's own rows keeps them), the next step's 8 x 8 block first.
-// Every pivot is the Schur complement's diagonal, as in the column-by-column
-// factorization.
-constexpr int kRowPitch = NB + 16;   // LDS row pitch (doubles) of the step's T rows
+// Sixteen steps of four columns; step s (rows and columns 4 s .. 4 s + 3:
+// register s % 4 of tile row s / 4):
+//   1. the step's 4 x 4 diagonal block t^T t, read from its lanes, is
+//      factored in every lane with the same float64 operations (pivot
+//      checks included) together with zt = t^{-T};
+//   2. the step's rows of A and of Z become zt times themselves, one MFMA
+//      per tile that adds (zt - I) times them in place (the rows of T, and
+//      of Z, are then final);
+//   3. the rows below take the rank-4 update A_IJ -= T_sI^T T_sJ and
+//      Z_IJ -= T_sI^T Z_sJ, one MFMA per tile, whose operands are the
+//      step's rows as they sit in the registers, the next step's diagonal
+//      tile first.  The accumulators are only ever updated whole.
+// No barrier and no LDS traffic inside the factorization: about 235 MFMAs
+// and the per-step 4 x 4 work on one SIMD.  Every pivot is the Schur
+// complement's diagonal, as in the column-by-column factorization.
+constexpr int kZPitch = NB + 1;   // LDS row pitch (doubles) of the transposed Z
+
+// f(std::integral_constant<int, i>) for i = B .. E - 1, each with i a
+// constant (so that register arrays stay indexed by constants)
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 __device__ __forceinline__ f64x4 mfma64(double a, double b, f64x4 c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
+// tile (I, J) of the upper (I <= J) and of the lower (J <= I) triangle
+__host__ __device__ constexpr int up_tile(int I, int J) { return I * 4 - I * (I - 1) / 2 + (J - I); }
+__host__ __device__ constexpr int lo_tile(int I, int J) { return I * (I + 1) / 2 + J; }
 
 // Factors diagonal block kb of matrix d (Dinv and Y_kk written to the
 // workspace).  A pivot fails when it is not above tol times the column's
 // original squared norm (or is not finite); returns false then, with
-// nothing written.  small: some pivot ratio was below kRatioTwo.
+// nothing written.  small: some pivot ratio was below kRatioTwo.  Called
+// by the whole workgroup; wavefront 0 factors, all threads store Dinv.
 __device__ __forceinline__ bool diag_block(const Launch& L, const MatDesc& d, int kb, double tol,
                                            bool& small, double* part) {
-  __shared__ double blk[8][8];                 // the step's 8 x 8 block (upper)
-  __shared__ double sdl[NB];                   // diag(S) of the block's columns
-  __shared__ double rows[8][kRowPitch];        // the step's 8 rows of T
-  __shared__ double ztl[kThreads / 64][8][8];  // zt, one copy per wavefront
+  __shared__ double zs[NB][kZPitch];   // Z transposed, for the Dinv stores
+  __shared__ double dsc[NB];           // D = diag(S)^{-1/2} of the block's columns
+  __shared__ int res[2];
   const int64_t rp = d.rp, o = static_cast<int64_t>(kb) * NB;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-  gptr<const double> A = to_global(dptr(L, d.oA) + o * rp + o);
-  f64x4 ta[4], tz[4];
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+    gptr<const double> A = to_global(dptr(L, d.oA) + o * rp + o);
+    const double sdv = dptr(L, d.oD)[NB * NB + o + lane];   // lane l: diag(S) of column l
+    dsc[lane] = rsqrt_nr(sdv);   // read back below by the same wavefront (in-order LDS)
+    double dr[4][4], dc[4];
 #pragma unroll
-  for (int I = 0; I < 4; ++I)
+    for (int I = 0; I < 4; ++I) {
+      dc[I] = dsc[16 * I + c];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 16 * I + 4 * v + g, col = 16 * w + c;
-      ta[I][v] = I <= w ? A[row * rp + col] : 0.0;
-      tz[I][v] = I >= w && row == col ? 1.0 : 0.0;
+      for (int v = 0; v < 4; ++v) dr[I][v] = dsc[16 * I + 4 * v + g];
     }
-  if (threadIdx.x < NB) sdl[threadIdx.x] = dptr(L, d.oD)[NB * NB + o + threadIdx.x];
-  if (lane == 0) {
+    f64x4 ta[10], tz[10];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int I = 0; I < 4; ++I)
 #pragma unroll
-      for (int j = i + 1; j < 8; ++j) ztl[w][i][j] = 0.0;
-  }
-  // the 8 x 8 block of step s, from registers 2 (s % 2) + h of tile
-  // (s / 2, s / 2) (held by wavefront s / 2)
-  auto put_block = [&](const f64x4& t, int s) {
-    const int c0 = 8 * (s % 2), v0 = 2 * (s % 2);
-    if (c >= c0 && c < c0 + 8) {
-      blk[g][c - c0] = t[v0];
-      blk[4 + g][c - c0] = t[v0 + 1];
-    }
-  };
-  if (w == 0) put_block(ta[0], 0);
-  __syncthreads();
-  bool sm = false;
+      for (int J = 0; J < 4; ++J)
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int S = s / 2, v0 = 2 * (s % 2);
-    // 1. t^T t = the 8 x 8 block: f holds t above the diagonal and
-    // zt = t^{-T} on and below it
-    double f[8][8], sk[8];
+        for (int v = 0; v < 4; ++v) {
+          if (I <= J)
+            ta[up_tile(I, J)][v] = A[(16 * I + 4 * v + g) * rp + 16 * J + c] * dr[I][v] * dc[J];
+          if (J <= I) tz[lo_tile(I, J)][v] = I == J && 4 * v + g == c ? 1.0 : 0.0;
+        }
+    bool ok = true, sm = false;
+    static_for<0, 16>([&](auto step) {
+      constexpr int s = decltype(step)::value, S = s / 4, v = s % 4;
+      // 1. the 4 x 4 block (element (k, j) in lane 16 k + 4 v + j) and its
+      // factor: f holds t above the diagonal, 1 / t_kk on it
+      double f[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sk[i] = sdl[8 * s + i];
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int j = i; j < 8; ++j) f[i][j] = blk[i][j];
-    }
-    bool ok = true;
+        for (int j = k; j < 4; ++j) f[k][j] = read_lane(ta[up_tile(S, S)][v], 16 * k + 4 * v + j);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const double dk = f[k][k];
-      ok = ok && dk > tol * sk[k] && dk < INFINITY;
-      sm = sm || !(dk >= kRatioTwo * sk[k]);
-      const double inv = rsqrt_nr(dk);
-      f[k][k] = inv;
+      for (int k = 0; k < 4; ++k) {
+        const double dk = f[k][k];   // the pivot ratio
+        ok = ok && dk > tol && dk < INFINITY;
+        sm = sm || !(dk >= kRatioTwo);
+        const double inv = rsqrt_nr(dk);
+        f[k][k] = inv;
 #pragma unroll
-      for (int j = k + 1; j < 8; ++j) f[k][j] *= inv;
+        for (int j = k + 1; j < 4; ++j) f[k][j] *= inv;
 #pragma unroll
-      for (int i = k + 1; i < 8; ++i)
+        for (int i = k + 1; i < 4; ++i)
 #pragma unroll
-        for (int j = i; j < 8; ++j) f[i][j] -= f[k][i] * f[k][j];
-    }
-    if (!ok) {
-      small = sm;
-      return false;   // the same in every thread
-    }
-#pragma unroll
-    for (int i = 1; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < i; ++j) {
-        double acc = 0.0;
-#pragma unroll
-        for (int m = j; m < i; ++m) acc += f[m][i] * (m == j ? f[j][j] : f[m][j]);
-        f[i][j] = -f[i][i] * acc;
+          for (int j = i; j < 4; ++j) f[i][j] -= f[k][i] * f[k][j];
       }
-    // the MFMA operand of zt: lane l holds zt[l % 16][4 h + l / 16]
+      // (a failed pivot is acted on after the loop: the factorization runs
+      // on through NaNs in registers, so that the loop stays one basic
+      // block and the scheduler can interleave the MFMAs with the next
+      // step's float64 work)
+      // zt = t^{-T} (lower triangular), then lane 16 g + c's operand
+      // zt[c][g] (zero outside the first four rows and above the diagonal)
+      double z[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i][i] = f[i][i];
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
+          double acc = 0.0;
+#pragma unroll
+          for (int m = j; m < i; ++m) acc += f[m][i] * z[m][j];
+          z[i][j] = -f[i][i] * acc;
+        }
+      }
+      // operand of the in-place row update: zt - I in rows 4 v .. 4 v + 3
+      // of the 16 x 4 operand (lane 16 g + c: row c, column g), zero
+      // elsewhere, so that one MFMA D = C + (zt - I) B leaves every other
+      // row of the tile as it is
+      double col[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        double x = z[3][j];
+#pragma unroll
+        for (int i = 2; i >= j; --i) x = c == 4 * v + i ? z[i][j] : x;
+        col[j] = x;
+      }
+      double op = col[3];
+#pragma unroll
+      for (int j = 2; j >= 0; --j) op = g == j ? col[j] : op;
+      const int ci = c - 4 * v;
+      op = ci >= 0 && ci < 4 && g <= ci ? op - (g == ci ? 1.0 : 0.0) : 0.0;
+      // 2. the step's rows (their entries left of the diagonal in the
+      // diagonal tile are not used below and not cleared)
+#pragma unroll
+      for (int J = S; J < 4; ++J) ta[up_tile(S, J)] = mfma64(op, ta[up_tile(S, J)][v], ta[up_tile(S, J)]);
+#pragma unroll
+      for (int J = 0; J <= S; ++J) tz[lo_tile(S, J)] = mfma64(op, tz[lo_tile(S, J)][v], tz[lo_tile(S, J)]);
+      if constexpr (s == 15) return;
+      // 3. rank-4 update; lane l's operand of T_sI is register v of tile
+      // (S, I) in lane l: T[4 s + l / 16][16 I + l % 16], cleared in tile
+      // row S for columns up to the step's (so that the step's rows and
+      // those above take no update, and the entries left of the diagonal
+      // are not read)
+      double a[4];
+#pragma unroll
+      for (int I = S; I < 4; ++I) {
+        const double x = -ta[up_tile(S, I)][v];
+        a[I] = I == S && c < 4 * v + 4 ? 0.0 : x;
+      }
+      const int Sn = (s + 1) / 4;
+      ta[up_tile(Sn, Sn)] = mfma64(a[Sn], ta[up_tile(S, Sn)][v], ta[up_tile(Sn, Sn)]);
+#pragma unroll
+      for (int I = S; I < 4; ++I)
+#pragma unroll
+        for (int J = I; J < 4; ++J)
+          if (!(I == Sn && J == Sn))
+            ta[up_tile(I, J)] = mfma64(a[I], ta[up_tile(S, J)][v], ta[up_tile(I, J)]);
+#pragma unroll
+      for (int I = S; I < 4; ++I)
+#pragma unroll
+        for (int J = 0; J <= S; ++J)
+          tz[lo_tile(I, J)] = mfma64(a[I], tz[lo_tile(S, J)][v], tz[lo_tile(I, J)]);
+    });
     if (lane == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j <= i; ++j) ztl[w][i][j] = f[i][j];
+      res[0] = ok ? 1 : 0;
+      res[1] = sm ? 1 : 0;
     }
-    asm volatile("" ::: "memory");   // lane 0's writes precede the reads (in-order LDS)
-    const double z0 = c < 8 ? ztl[w][c][g] : 0.0;
-    const double z1 = c < 8 ? ztl[w][c][4 + g] : 0.0;
-    // 2. the step's rows of A (tile (S, w), w >= S) and of Z (w <= S)
-    const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
-    if (w >= S) {
-      f64x4 r = mfma64(z0, ta[S][v0], zero);
-      r = mfma64(z1, ta[S][v0 + 1], r);
-      double x0 = r[0], x1 = r[1];
-      if (w == S) {   // T is upper triangular: exact zeros left of the diagonal
-        if (c < 8 * (s % 2) + g) x0 = 0.0;
-        if (c < 8 * (s % 2) + 4 + g) x1 = 0.0;
+    if (ok) {
+      // Y_kk = Z (lower, zeros above), Z^T staged in LDS for Dinv, and this
+      // block's share of trace(C^{-1}): S_cc Y_jc^2 over its columns c < r
+      gptr<double> Y = to_global(dptr(L, d.oY) + o * rp + o);
+      double tr = 0.0;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        double q = 0.0;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = 16 * I + 4 * v + g, cl = 16 * J + c;
+            const double zv = J <= I ? tz[lo_tile(I, J)][v] * dc[J] : 0.0;
+            Y[row * rp + cl] = zv;
+            zs[cl][row] = zv;
+            q += zv * zv;
+          }
+        const int cl = 16 * J + c;
+        const double sd = __shfl(sdv, cl);
+        tr += o + cl < d.r ? sd * q : 0.0;
       }
-      ta[S][v0] = x0;
-      ta[S][v0 + 1] = x1;
-      rows[g][16 * w + c] = x0;
-      rows[4 + g][16 * w + c] = x1;
-    }
-    if (w <= S) {
-      f64x4 r = mfma64(z0, tz[S][v0], zero);
-      r = mfma64(z1, tz[S][v0 + 1], r);
-      tz[S][v0] = r[0];
-      tz[S][v0 + 1] = r[1];
-    }
-    __syncthreads();
-    if (s == 7) break;
-    // 3. rank-8 update of the rows below the step's: lane l's operand of
-    // T_sI is T[8 s + 4 h + l / 16][16 I + l % 16]
-    auto update = [&](f64x4& t, int I, const f64x4& bsrc) {
-      // (t and bsrc are the same tile when I == S: operands first)
-      const double a0 = -rows[g][16 * I + c], a1 = -rows[4 + g][16 * I + c];
-      const double b0 = bsrc[v0], b1 = bsrc[v0 + 1];
-      const double keep0 = t[v0], keep1 = t[v0 + 1];
-      t = mfma64(a0, b0, t);
-      t = mfma64(a1, b1, t);
-      if (I == S) {   // the step's own rows stay as they are
-        t[v0] = keep0;
-        t[v0 + 1] = keep1;
-      }
-    };
-    const int Sn = (s + 1) / 2;
-    if (w == Sn) {   // the next step's block first
-      update(ta[Sn], Sn, ta[S]);
-      put_block(ta[Sn], s + 1);
-    }
 #pragma unroll
-    for (int I = S; I < 4; ++I)
-      if (I <= w && !(w == Sn && I == Sn)) update(ta[I], I, ta[S]);
-    if (w <= S) {
-#pragma unroll
-      for (int I = S; I < 4; ++I) update(tz[I], I, tz[S]);
+      for (int m = 32; m >= 1; m >>= 1) tr += __shfl_xor(tr, m);
+      if (part && lane == 0) *part = tr;
     }
-    __syncthreads();
   }
-  small = sm;
-  // Dinv = T_kk^{-1} = Z^T (upper triangular), Y_kk = Z (lower, zeros above).
-  gptr<double> Dinv = to_global(dptr(L, d.oD));
-  gptr<double> Y = to_global(dptr(L, d.oY) + o * rp + o);
-  double q = 0.0;
+  __syncthreads();
+  const bool ok = res[0] != 0;
+  small = res[1] != 0;
+  if (ok) {   // Dinv = T_kk^{-1} = Z^T (upper triangular), row-major
+    gptr<double> Dinv = to_global(dptr(L, d.oD));
 #pragma unroll
-  for (int I = 0; I < 4; ++I)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 16 * I + 4 * v + g, col = 16 * w + c;
-      const double z = I >= w ? tz[I][v] : 0.0;
-      Dinv[col * NB + row] = z;
-      Y[row * rp + col] = z;
-      q += z * z;
-    }
-  if (part) {
-    // this block's share of trace(C^{-1}): S_cc Y_jc^2 over its columns c < r
-    const int col = 16 * w + c;
-    const double wt = o + col < d.r ? sdl[col] : 0.0;
-    const double t = block_sum(wt * q);
-    if (threadIdx.x == 0) *part = t;
+    for (int e = threadIdx.x; e < NB * NB; e += kThreads) Dinv[e] = zs[e / NB][e % NB];
   }
-  return true;
+  __syncthreads();   // the shared buffers are free for the next call
+  return ok;
 }
 
 // Diagonal block step of the first pass (one workgroup per matrix).
