@@ -153,7 +153,7 @@ __device__ __forceinline__ void for_items(const Launch& L, F&& body) {
 // Workgroups of a launch whose kernel loops over its work items: launches
 // that only some matrices need (gates kGateRetry and kGateTwo) run at most
 // this many, so that they cost little when no matrix needs them.
-constexpr int kGatedGrid = 1024;
+constexpr int kGatedGrid = 256;
 inline __host__ __device__ int gated_grid(int total) { return total < kGatedGrid ? total : kGatedGrid; }
 
 // Grouped tile order inside one matrix's tx x ty tile grid: consecutive

@@ -243,11 +243,12 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     k.s_cn = cdiv(k.n, k.kl_cn);
   }
   // Workspace: status words (one per matrix, then the union of the control
-  // bits of the factorization in progress) | matrix table (grouped calls) |
-  // per-matrix buffers.
+  // bits of the factorization in progress, then the dataflow
+  // factorization's counters) | matrix table (grouped calls) | per-matrix
+  // buffers.
   size_t off = 0;
   p.status_off = off;
-  off = align_up(off + static_cast<size_t>(count + 1) * 4);
+  off = align_up(off + static_cast<size_t>(count + 1 + kFlowWords) * 4);
   p.table_off = off;
   if (!single) off = align_up(off + static_cast<size_t>(count) * sizeof(MatDesc));
   p.table.resize(count);
@@ -283,9 +284,11 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     d.oS = take(static_cast<size_t>(std::max(k.s_gp, k.s_gw)) * rp * rp * 8);
     d.oA = take(rp * rp * 8);
     d.oY = take(rp * rp * 8);
-    // diagonal-block inverse, diag(S), then the trace partials of the
-    // first pass (one per 64 x 64 block of T^{-T})
-    d.oD = take((kCholNB * kCholNB + rp + (rp / kCholNB) * (rp / kCholNB)) * 8);
+    // diagonal-block inverse, diag(S), the trace partials of the first
+    // pass (one per 64 x 64 block of T^{-T}), then the dataflow flags (one
+    // word per 64 x 64 block)
+    const size_t nbk = (rp / kCholNB) * (rp / kCholNB);
+    d.oD = take((kCholNB * kCholNB + rp + nbk) * 8 + nbk * 4);
     d.oN = take(r * 4);
     const size_t kpart = std::max(k.s_mv > 1 ? k.s_mv * m * r : 0, k.s_mtu > 1 ? k.s_mtu * n * r : 0);
     d.oK = kpart ? take(kpart * 4) : 0;
@@ -454,48 +457,66 @@ hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
   // caller forms between stages, so its single pass is final.
   base.retry = p.sharded && which == 0 ? 0 : 1;
   base.gate = kGateAll;   // k_chol_init clears the control bits
-  int max_nblk = 0;
-  for (const ClassRec& c : p.cls) max_nblk = std::max(max_nblk, c.rp / kCholNB);
   DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
     const int nb = c.rp / kCholNB;
     ci.splits = which == 0 ? c.s_gp : c.s_gw;
     ci.tiles = nb * (nb + 1) / 2 * kCholInitParts;
     return true;
   }, [&](const Launch& L) { return launch_chol_init(L, st); }));
-  // block steps in pairs (kb, kb + 1) with look-ahead: factor kb, bring
-  // block row kb + 1 up to date, factor kb + 1, then one trailing pass with
-  // both panels
-  auto diag_panel = [&](int kb) -> hipError_t {
-    base.kb = kb;
-    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-      ci.tiles = c.rp / kCholNB > kb ? 1 : 0;
-      return true;
-    }, [&](const Launch& L) { return launch_chol_diag(L, st); }));
-    return grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-      const int nb = c.rp / kCholNB;
-      ci.tiles = nb > kb ? nb - 1 : 0;
-      return true;
-    }, [&](const Launch& L) { return launch_chol_panel(L, st); });
-  };
+  // Every block step in one dataflow launch (k_chol_flow) when its work
+  // items, one workgroup per 64 x 64 block of T and of Y, all fit the chip
+  // at once (its kernel holds one workgroup per CU); otherwise a launch per
+  // step, each of which fills the chip.
+  int flow_items = 0, max_nblk = 0;
+  for (const ClassRec& c : p.cls) {
+    if (c.small_rb > 0) continue;
+    const int nb = c.rp / kCholNB;
+    flow_items += c.count * nb * nb;
+    max_nblk = std::max(max_nblk, nb);
+  }
   base.gate = kGateFirst;
-  for (int kb = 0; kb < max_nblk; kb += 2) {
-    DION_TRY(diag_panel(kb));
-    if (kb + 1 >= max_nblk) break;
-    base.kb = kb;
-    base.mode = 1;
+  if (flow_items <= kFlowItems) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-      const int nl = c.rp / kCholNB - kb - 1;
-      ci.tiles = nl > 0 ? nl + kb + 1 : 0;
+      const int nb = c.rp / kCholNB;
+      ci.tx = nb;
+      ci.tiles = nb * nb;
       return true;
-    }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
-    DION_TRY(diag_panel(kb + 1));
-    base.kb = kb;
-    base.mode = 2;
-    DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
-      const int nl = c.rp / kCholNB - kb - 2;
-      ci.tiles = nl > 0 ? nl * (nl + 1) / 2 + nl * (kb + 2) : 0;
-      return true;
-    }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
+    }, [&](const Launch& L) { return launch_chol_flow(L, st); }));
+  } else {
+    // block steps in pairs (kb, kb + 1) with look-ahead: factor kb, bring
+    // block row kb + 1 up to date, factor kb + 1, then one trailing pass
+    // with both panels
+    auto diag_panel = [&](int kb) -> hipError_t {
+      base.kb = kb;
+      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+        ci.tiles = c.rp / kCholNB > kb ? 1 : 0;
+        return true;
+      }, [&](const Launch& L) { return launch_chol_diag(L, st); }));
+      return grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+        const int nb = c.rp / kCholNB;
+        ci.tiles = nb > kb ? nb - 1 : 0;
+        return true;
+      }, [&](const Launch& L) { return launch_chol_panel(L, st); });
+    };
+    for (int kb = 0; kb < max_nblk; kb += 2) {
+      DION_TRY(diag_panel(kb));
+      if (kb + 1 >= max_nblk) break;
+      base.kb = kb;
+      base.mode = 1;
+      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+        const int nl = c.rp / kCholNB - kb - 1;
+        ci.tiles = nl > 0 ? nl + kb + 1 : 0;
+        return true;
+      }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
+      DION_TRY(diag_panel(kb + 1));
+      base.kb = kb;
+      base.mode = 2;
+      DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
+        const int nl = c.rp / kCholNB - kb - 2;
+        ci.tiles = nl > 0 ? nl * (nl + 1) / 2 + nl * (kb + 2) : 0;
+        return true;
+      }, [&](const Launch& L) { return launch_chol_trail(L, st); }));
+    }
   }
   if (base.retry) {   // the decision whether more passes follow
     DION_TRY(grouped(p, base, [&](const ClassRec&, ClassInfo& ci) {

@@ -22,6 +22,10 @@ constexpr int kSmallFactorFloats = 16384;
 constexpr int kSmallResidentFloats = 39680;
 // Grouped launches carry at most this many shape classes.
 constexpr int kMaxClasses = 8;
+// Status words after the per-matrix ones and their union: the dataflow
+// factorization's ticket counter, its count of finished tasks, and its
+// abort word (a wait that ran out).
+constexpr int kFlowWords = 3;
 
 // Sliced Gram matrix.  Each column of the factor Q is scaled by a power of
 // two 2^-e into (-1, 1) and written as kQDigits signed base-2^7 digits

@@ -41,12 +41,13 @@ __device__ __forceinline__ double* dptr(const Launch& L, int64_t off) {
   return reinterpret_cast<double*>(L.ws + off);
 }
 
-// C += L^T R for 64 x 64 blocks over 64 reduction rows, C[i][j] +=
+// C += L^T R (NEG: C -= L^T R) for 64 x 64 blocks over 64 reduction rows, C[i][j] +=
 // sum_e L[e][i] R[e][j] (L, R row-major with pitches ll, lr), on the
 // 16 x 16 x 4 float64 MFMA: 2 x 2 wavefronts of 32 x 32, each lane loading
 // its own operands from memory (lane l: row 4 s + l / 16, column l % 16 of
 // a 16-wide column strip, 16 consecutive doubles per 16 lanes).  All loads
 // of a wavefront are issued before its first MFMA.
+template <bool NEG = false>
 __device__ __forceinline__ void block_tn_add(const double* Lp, int64_t ll, const double* Rp,
                                              int64_t lr, f64x4 (&acc)[2][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -60,6 +61,7 @@ __device__ __forceinline__ void block_tn_add(const double* Lp, int64_t ll, const
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       a[s][f] = L[(4 * s + g) * ll + ci + 16 * f];
+      if constexpr (NEG) a[s][f] = -a[s][f];
       b[s][f] = R[(4 * s + g) * lr + cj + 16 * f];
     }
 #pragma unroll
@@ -90,6 +92,15 @@ __device__ __forceinline__ int64_t block_off(int fm, int fn, int v, int64_t ld) 
   return row * ld + col;
 }
 
+// Dataflow flags of matrix d (one launch for the whole factorization,
+// k_chol_flow): nb x nb words after its trace partials; word (i, j), i <= j:
+// block (i, j) of T is final (for i = j: Dinv_i and Y_ii are written);
+// word (i, c), c < i: block (i, c) of Y is final.
+__device__ __forceinline__ int* flow_flags(const Launch& L, const MatDesc& d) {
+  const int nb = d.rp / NB;
+  return reinterpret_cast<int*>(dptr(L, d.oD) + NB * NB + d.rp + nb * nb);
+}
+
 // A = the Gram matrix (the sum of its reduction slices' partials, upper
 // triangle, mirrored), rows past r padded with the identity; diag(S) kept
 // aside.  Work item: a quarter (16 rows) of one 64 x 64 upper block; each
@@ -102,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
   int local;
   // A factorization starts with no control bits (no other kernel of this
   // launch reads them), in the matrices' words and in their union
-  if (blockIdx.x == 0 && threadIdx.x == 0) L.status[L.any_slot] = 0;
+  // and the dataflow factorization's counters
+  if (blockIdx.x == 0 && threadIdx.x < 1 + kFlowWords) L.status[L.any_slot + threadIdx.x] = 0;
   locate(L, xcd_remap(blockIdx.x, gridDim.x), d, ci, local);
   if (skipped(L, d)) return;
   if (local == 0 && threadIdx.x == 0) L.status[d.slot] &= kStatusMask;
@@ -114,6 +126,11 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
     ++bi;
   }
   const int bj = bi + p;
+  if (quarter == 0 && threadIdx.x == 0) {   // the blocks' dataflow flags
+    int* fl = flow_flags(L, d);
+    fl[bi * nblk + bj] = 0;
+    fl[bj * nblk + bi] = 0;
+  }
   gptr<const double> S = to_global(reinterpret_cast<const double*>(L.ws + d.oS));
   double* A = dptr(L, d.oA);
   double* Sd = dptr(L, d.oD) + NB * NB;
@@ -216,9 +233,10 @@ __host__ __device__ constexpr int lo_tile(int I, int J) { return I * (I + 1) / 2
 // workspace).  A pivot fails when it is not above tol times the column's
 // original squared norm (or is not finite); returns false then, with
 // nothing written.  small: some pivot ratio was below kRatioTwo.  Called
-// by the whole workgroup; wavefront 0 factors, all threads store Dinv.
+// by the whole workgroup; wavefront 0 factors, all threads store Dinv
+// (row-major, row pitch ldd, at dinv).
 __device__ __forceinline__ bool diag_block(const Launch& L, const MatDesc& d, int kb, double tol,
-                                           bool& small, double* part) {
+                                           bool& small, double* part, double* dinv, int64_t ldd) {
   __shared__ double zs[NB][kZPitch];   // Z transposed, for the Dinv stores
   __shared__ double dsc[NB];           // D = diag(S)^{-1/2} of the block's columns
   __shared__ int res[2];
@@ -372,9 +390,9 @@ __device__ __forceinline__ bool diag_block(const Launch& L, const MatDesc& d, in
   const bool ok = res[0] != 0;
   small = res[1] != 0;
   if (ok) {   // Dinv = T_kk^{-1} = Z^T (upper triangular), row-major
-    gptr<double> Dinv = to_global(dptr(L, d.oD));
+    gptr<double> Dinv = to_global(dinv);
 #pragma unroll
-    for (int e = threadIdx.x; e < NB * NB; e += kThreads) Dinv[e] = zs[e / NB][e % NB];
+    for (int e = threadIdx.x; e < NB * NB; e += kThreads) Dinv[(e / NB) * ldd + e % NB] = zs[e / NB][e % NB];
   }
   __syncthreads();   // the shared buffers are free for the next call
   return ok;
@@ -398,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
   if (skipped(L, d)) return;
   bool small;
   const bool ok = diag_block(L, d, L.kb, L.retry ? kRatioRetry : kRatioTwo, small,
-                             trace_part(L, d, L.kb, L.kb));
+                             trace_part(L, d, L.kb, L.kb), dptr(L, d.oD), NB);
   if (threadIdx.x == 0) {
     const int32_t bits = !ok ? (L.retry ? (kCtlRetry | kCtlTwo) : L.flag)
                              : (small && L.retry ? kCtlTwo : 0);
@@ -406,6 +424,188 @@ __global__ __launch_bounds__(kThreads) void k_chol_diag(Launch L) {
       atomicOr(&L.status[d.slot], bits);
       if (bits & (kCtlRetry | kCtlTwo)) atomicOr(&L.status[L.any_slot], bits);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The first-pass factorization in one launch.  Work items are the 64 x 64
+// blocks of T (upper triangle, in A's storage) and of Y = T^{-T} (strictly
+// lower triangle), one workgroup each, in block-row order over all
+// matrices: row i of a matrix is its diagonal block, then the blocks (i, j)
+// of T, j > i, then the blocks (i, c) of Y, c < i.  Every block reads only
+// blocks of earlier rows and the diagonal block of its own row, and sums
+// its whole update before it is written (left-looking):
+//   diagonal (i, i):  A_ii - sum_{k<i} T_ki^T T_ki, then diag_block
+//                     (Dinv_i stored in place of A_ii, Y_ii, the trace
+//                     partial, the pivot decisions);
+//   T (i, j):         T_ij = Dinv_i^T (A_ij - sum_{k<i} T_ki^T T_kj);
+//   Y (i, c):         Y_ic = -Dinv_i^T sum_{k=c}^{i-1} T_ki^T Y_kc (Y_cc is
+//                     the diagonal block c's).
+// This is the arithmetic of k_chol_diag / k_chol_panel / k_chol_trail in
+// another order of the same sums.  A workgroup takes its item from a
+// ticket counter when it starts, so every item it waits on is held by a
+// workgroup that started before it: the waits end however many workgroups
+// are resident.  A block's flag is set with an agent-scope release after
+// its stores; a reader polls it with an agent-scope acquire (the L2 caches
+// of the XCDs are not coherent) before it loads the block.  A wait gives up
+// after kFlowWait ticks of the 100 MHz wall clock (0.2 s, far beyond any
+// factorization here) or kFlowSpin polls, whichever comes first: it flags
+// its matrix broken down and sets the abort
+// word, after which every wait of the launch returns at once; the launch
+// then still ends, its results are not used, and the step reports the
+// breakdown.  The last workgroup to finish resets the counters for the
+// next launch.
+constexpr int64_t kFlowWait = 20000000;   // wall-clock ticks
+constexpr int kFlowSpin = 1 << 24;        // polls of at least 64 cycles each
+
+__device__ __forceinline__ void flow_wait(const Launch& L, const MatDesc& d, const int* f) {
+  if (threadIdx.x == 0) {
+    int32_t* abort_w = L.status + L.any_slot + 3;
+    const int64_t t0 = static_cast<int64_t>(wall_clock64());
+    for (int n = 0; __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0; ++n) {
+      if (n >= kFlowSpin || static_cast<int64_t>(wall_clock64()) - t0 > kFlowWait ||
+          __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        __hip_atomic_store(abort_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        atomicOr(&L.status[d.slot], L.flag);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void flow_signal(int* f) {
+  __syncthreads();   // every wavefront's stores are issued
+  if (threadIdx.x == 0) {
+    __threadfence();
+    __hip_atomic_store(f, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ __forceinline__ void load_block(const double* p, int64_t ld, f64x4 (&acc)[2][2]) {
+  gptr<const double> q = to_global(p);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[fm][fn][v] = q[block_off(fm, fn, v, ld)];
+}
+
+__device__ __forceinline__ void store_block(double* p, int64_t ld, const f64x4 (&acc)[2][2],
+                                            double sign = 1.0) {
+  gptr<double> q = to_global(p);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) q[block_off(fm, fn, v, ld)] = sign * acc[fm][fn][v];
+}
+
+__global__ __launch_bounds__(kThreads) void k_chol_flow(Launch L) {
+  __shared__ int ticket;
+  int32_t* words = L.status + L.any_slot;   // [1] ticket, [2] finished items, [3] abort
+  if (threadIdx.x == 0) ticket = atomicAdd(&words[1], 1);
+  __syncthreads();
+  // the item: block row i of its matrix, position pos in that row; each
+  // row of a matrix with nb blocks a side has nb items
+  int t = ticket, i = 0, pos = 0, mi = -1, nb = 0;
+  for (;;) {
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) {
+      if (mi >= 0 || c >= L.nclass) continue;
+      const int nbc = L.cls[c].tx;
+      if (nbc <= i) continue;
+      const int seg = L.cls[c].count * nbc;
+      if (t < seg) {
+        mi = L.cls[c].first + t / nbc;
+        nb = nbc;
+        pos = t % nbc;
+      } else {
+        t -= seg;
+      }
+    }
+    if (mi >= 0 || i >= 63) break;
+    ++i;
+  }
+  if (mi >= 0) {
+    const MatDesc d = L.table ? L.table[mi] : L.inl;
+    const int64_t rp = d.rp;
+    double* A = dptr(L, d.oA);
+    double* Y = dptr(L, d.oY);
+    int* fl = flow_flags(L, d);
+    auto blk = [&](double* base, int r, int c) { return base + static_cast<int64_t>(r) * NB * rp + c * NB; };
+    f64x4 acc[2][2], out[2][2];
+    if (pos < nb - i) {   // block (i, j) of T
+      const int j = i + pos;
+      load_block(blk(A, i, j), rp, acc);
+      for (int k = 0; k < i; ++k) {
+        flow_wait(L, d, &fl[k * nb + i]);
+        if (j != i) flow_wait(L, d, &fl[k * nb + j]);
+        block_tn_add<true>(blk(A, k, i), rp, blk(A, k, j), rp, acc);
+      }
+      store_block(blk(A, i, j), rp, acc);
+      if (j == i) {
+        __syncthreads();   // the block is in memory for diag_block
+        bool small;
+        const bool ok = diag_block(L, d, i, L.retry ? kRatioRetry : kRatioTwo, small,
+                                   trace_part(L, d, i, i), blk(A, i, i), rp);
+        if (threadIdx.x == 0) {
+          const int32_t bits = !ok ? (L.retry ? (kCtlRetry | kCtlTwo) : L.flag)
+                                   : (small && L.retry ? kCtlTwo : 0);
+          if (bits) {
+            atomicOr(&L.status[d.slot], bits);
+            if (bits & (kCtlRetry | kCtlTwo)) atomicOr(&L.status[L.any_slot], bits);
+          }
+        }
+      } else {
+        flow_wait(L, d, &fl[i * nb + i]);   // (its barrier also orders the stores above)
+        block_tn(blk(A, i, i), rp, blk(A, i, j), rp, out);
+        __syncthreads();   // every wavefront has read the block before any writes it
+        store_block(blk(A, i, j), rp, out);
+      }
+      flow_signal(&fl[i * nb + j]);
+    } else {   // block (i, c) of Y
+      const int c = pos - (nb - i);
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = f64x4{0.0, 0.0, 0.0, 0.0};
+      for (int k = c; k < i; ++k) {
+        flow_wait(L, d, &fl[k * nb + i]);
+        flow_wait(L, d, &fl[k * nb + c]);   // Y_kc (the diagonal block c for k = c)
+        block_tn_add(blk(A, k, i), rp, blk(Y, k, c), rp, acc);
+      }
+      store_block(blk(Y, i, c), rp, acc);
+      flow_wait(L, d, &fl[i * nb + i]);
+      block_tn(blk(A, i, i), rp, blk(Y, i, c), rp, out);
+      __syncthreads();   // every wavefront has read the block before any writes it
+      store_block(blk(Y, i, c), rp, out, -1.0);
+      // block (i, c) of Y is final: its share of trace(C^{-1})
+      const double* sd = dptr(L, d.oD) + NB * NB + c * NB;
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      double tq = 0.0;
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn) {
+        const int col = (wave & 1) * 32 + fn * 16 + (lane & 15);
+        double q = 0.0;
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) q += out[fm][fn][v] * out[fm][fn][v];
+        tq += c * NB + col < d.r ? sd[col] * q : 0.0;
+      }
+      tq = block_sum(tq);
+      if (threadIdx.x == 0) *trace_part(L, d, i, c) = tq;
+      flow_signal(&fl[i * nb + c]);
+    }
+  }
+  if (threadIdx.x == 0 && atomicAdd(&words[2], 1) == static_cast<int>(gridDim.x) - 1) {
+    words[1] = 0;   // every item has finished: counters for the next launch
+    words[2] = 0;
+    words[3] = 0;
   }
 }
 
@@ -607,7 +807,7 @@ __global__ __launch_bounds__(kThreads) void k_chol_one(Launch L) {
     bool failed = false;
     for (int kb = 0; kb < nblk; ++kb) {
       bool small;
-      if (!diag_block(L, d, kb, tol, small, nullptr)) {
+      if (!diag_block(L, d, kb, tol, small, nullptr, dptr(L, d.oD), NB)) {
         failed = true;
         break;
       }
@@ -740,6 +940,7 @@ hipError_t launch_chol_init(const Launch& L, hipStream_t st) { return go(k_chol_
 hipError_t launch_chol_diag(const Launch& L, hipStream_t st) { return go(k_chol_diag, L, st); }
 hipError_t launch_chol_panel(const Launch& L, hipStream_t st) { return go(k_chol_panel, L, st); }
 hipError_t launch_chol_trail(const Launch& L, hipStream_t st) { return go(k_chol_trail, L, st); }
+hipError_t launch_chol_flow(const Launch& L, hipStream_t st) { return go(k_chol_flow, L, st); }
 hipError_t launch_chol_one(const Launch& L, hipStream_t st) { return go_capped(k_chol_one, L, st); }
 hipError_t launch_orth_decide(const Launch& L, hipStream_t st) { return go(k_orth_decide, L, st); }
 hipError_t launch_trmm64(const Launch& L, hipStream_t st) { return go_capped(k_trmm64, L, st); }

@@ -28,6 +28,14 @@ hipError_t launch_chol_init(const Launch& L, hipStream_t st);
 hipError_t launch_chol_diag(const Launch& L, hipStream_t st);
 hipError_t launch_chol_panel(const Launch& L, hipStream_t st);
 hipError_t launch_chol_trail(const Launch& L, hipStream_t st);
+// the whole first-pass factorization (what k_chol_diag, k_chol_panel and
+// k_chol_trail do over all block steps) in one launch: one workgroup per
+// 64 x 64 block of T and of Y (ClassInfo: tx = blocks per side, tiles =
+// tx * tx), ordered by block row, each waiting on the blocks it reads
+hipError_t launch_chol_flow(const Launch& L, hipStream_t st);
+// the most work items (blocks of T and of Y over the launch) for which the
+// factorization takes k_chol_flow: those of one workgroup per CU
+constexpr int kFlowItems = 256;
 // the whole factorization of each matrix in one workgroup (shifted retry,
 // second pass) and the float64 triangular multiply that follows it
 hipError_t launch_chol_one(const Launch& L, hipStream_t st);

@@ -222,3 +222,33 @@ def test_batched_mixed_block_counts(gpu_lib, variant, arith):
     for c, (m, n, r) in zip(cases, shapes):
         res, x_prev = c.oracle(variant)
         assert_close(c.errors(x_prev, res.M), TOL_1, f"mixed {m}x{n} r={r} {variant} {arith}")
+
+
+# The same classes six times over (306 blocks of T and Y: more than the
+# one-launch factorization takes, so the launch-per-step chain runs): every
+# copy of a matrix has the inputs of the first, whose step is checked
+# against the oracle, and must come out bitwise equal to it.
+@pytest.mark.parametrize("variant", [ORTH, DION])
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+def test_batched_mixed_block_counts_chain(gpu_lib, variant, arith):
+    import torch
+    shapes = [(400, 300, 150), (256, 192, 48), (700, 650, 300), (300, 260, 250)]
+    blocks = sum((r + 63) // 64 * ((r + 63) // 64) for _, _, r in shapes)
+    copies = 6
+    assert copies * blocks > 256
+    cases = [Case(_wl(m, n, r, "bf16", seed=80 + i), MatrixSpec(0, "W", 0, m, n, r))
+             for i, (m, n, r) in enumerate(shapes)]
+    for c in cases:
+        c.load_grad(0)
+    extra = [[(c.X.clone(), c.G, c.R.clone(), c.V.clone()) for c in cases] for _ in range(copies - 1)]
+    say(f"mixed block counts, chain {variant} {arith}")
+    mats = [(c.X, c.G, c.R, c.V) for c in cases] + [t for e in extra for t in e]
+    ws = gpu_lib.step_batched(mats, 0.01, 0.95, variant, math=arith)
+    assert gpu_lib.status(ws, len(mats))[0] == 0
+    torch.cuda.synchronize()
+    for c, (m, n, r) in zip(cases, shapes):
+        res, x_prev = c.oracle(variant)
+        assert_close(c.errors(x_prev, res.M), TOL_1, f"mixed chain {m}x{n} r={r} {variant} {arith}")
+    for e in extra:
+        for c, (x, _, rr, v) in zip(cases, e):
+            assert torch.equal(x, c.X) and torch.equal(rr, c.R) and torch.equal(v, c.V)
