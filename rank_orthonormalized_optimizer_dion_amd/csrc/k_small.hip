@@ -258,57 +258,124 @@ __device__ __forceinline__ void small_gram(OrthLds& sh, const float* Q, int rows
   __syncthreads();
 }
 
-// Step K of small_chol and the steps after it, one instantiation per step,
-// so that every index into v is a constant (v stays in registers).  Row K
-// of T is broadcast by reading lane i's value for each i > K (no LDS round
-// trip on the factorization's serial path).
-template <int RB, int K>
-__device__ __forceinline__ void chol_steps(OrthLds& sh, double (&v)[RB], int r, double tol,
-                                           int c, bool za, bool& bad, bool& small) {
-  if constexpr (K < RB) {
-    const double dk = read_lane(v[K], K);
-    if (K < r) {
-      const double sk = sh.s[K][K];
-      bad = bad || !(dk > tol * sk && dk < INFINITY);
-      small = small || !(dk >= kRatioTwo * sk);
-    }
-    const double inv = rsqrt_nr(dk);
-    v[K] = za ? (c <= K ? v[K] * inv : 0.0) : (c > K ? v[K] * inv : (c == K ? dk * inv : 0.0));
-#pragma unroll
-    for (int i = K + 1; i < RB; ++i) v[i] -= read_lane(v[K], i) * v[K];
-    chol_steps<RB, K + 1>(sh, v, r, tol, c, za, bad, small);
+// f(std::integral_constant<int, i>) for i = B .. E - 1, each with i a
+// constant (so that register values stay indexed by constants)
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
+__device__ __forceinline__ f64x4 mfma64(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// T^{-1} (into tinv), the trace of C^{-1} (C the column-scaled Gram matrix)
+// and the pivot decisions for A = S + shift diag(S) (rows and columns past
+// r: the identity), on wavefront 0.  A pivot fails (bad) when its ratio
+// d_k / S_kk is not above tol or is not finite; small: some ratio is below
+// kRatioTwo.  A is scaled to A' = D A D, D = diag(S)^{-1/2}, so that its
+// pivots are those ratios; A' and Z' = T'^{-T} (T' = T D, Z = Z' D) are
+// one 16 x 16 float64 MFMA accumulator each (register v of lane 16 g + c:
+// row 4 v + g, column c), factored in steps of four columns: the step's
+// 4 x 4 block, read from its lanes, is factored alike in every lane
+// together with zt = t^{-T}; one MFMA adds (zt - I) times the step's rows
+// to them in place (rows of T' and of Z' final); one more per tile makes
+// the rank-4 update of the rows below (the operand cleared up to the
+// step's columns, so that those rows take none).
 template <int RB>
 __device__ __forceinline__ void small_chol(OrthLds& sh, int r, double shift, double tol) {
   __syncthreads();   // every thread has read the previous factorization's results
   if (threadIdx.x < 64) {
-    const int lane = threadIdx.x, c = lane & 31;
-    const bool za = lane >= 32;
-    double v[RB];
+    const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+    const double sc = c < r ? rsqrt_nr(sh.s[c][c]) : 1.0;   // D of the lane's column
+    f64x4 ta, tz;
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      double x = i == c ? 1.0 : 0.0;
-      if (!za && i < r && c < r) x = sh.s[i][c] + (i == c ? shift * sh.s[i][i] : 0.0);
-      v[i] = x;
-    }
-    bool bad = false, small = false;
-    chol_steps<RB, 0>(sh, v, r, tol, c, za, bad, small);
-    double tr = 0.0;
-    if (za && c < RB) {
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        sh.tinv[c][i] = v[i];
-        tr = fma(v[i], v[i], tr);
+    for (int v = 0; v < 4; ++v) {
+      const int row = 4 * v + g;
+      double a = row == c ? 1.0 : 0.0;
+      if (row < r && c < r) {
+        const double sr = rsqrt_nr(sh.s[row][row]);
+        a = (sh.s[row][c] + (row == c ? shift * sh.s[row][row] : 0.0)) * sr * sc;
       }
-      tr = c < r ? sh.s[c][c] * tr : 0.0;
+      ta[v] = a;
+      tz[v] = row == c ? 1.0 : 0.0;
     }
+    bool ok = true, sm = false;
+    static_for<0, RB / 4>([&](auto step) {
+      constexpr int v = decltype(step)::value;
+      double f[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int j = k; j < 4; ++j) f[k][j] = read_lane(ta[v], 16 * k + 4 * v + j);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const double dk = f[k][k];   // the pivot ratio
+        if (4 * v + k < r) {
+          ok = ok && dk > tol && dk < INFINITY;
+          sm = sm || !(dk >= kRatioTwo);
+        }
+        const double inv = rsqrt_nr(dk);
+        f[k][k] = inv;
+#pragma unroll
+        for (int j = k + 1; j < 4; ++j) f[k][j] *= inv;
+#pragma unroll
+        for (int i = k + 1; i < 4; ++i)
+#pragma unroll
+          for (int j = i; j < 4; ++j) f[i][j] -= f[k][i] * f[k][j];
+      }
+      double z[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i][i] = f[i][i];
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
+          double acc = 0.0;
+#pragma unroll
+          for (int m = j; m < i; ++m) acc += f[m][i] * z[m][j];
+          z[i][j] = -f[i][i] * acc;
+        }
+      }
+      // lane 16 g + c's operand: zt[c - 4 v][g] - [c - 4 v == g] in rows
+      // 4 v .. 4 v + 3 of the 16 x 4 operand, zero elsewhere
+      double col[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        double x = z[3][j];
+#pragma unroll
+        for (int i = 2; i >= j; --i) x = c == 4 * v + i ? z[i][j] : x;
+        col[j] = x;
+      }
+      double op = col[3];
+#pragma unroll
+      for (int j = 2; j >= 0; --j) op = g == j ? col[j] : op;
+      const int ci = c - 4 * v;
+      op = ci >= 0 && ci < 4 && g <= ci ? op - (g == ci ? 1.0 : 0.0) : 0.0;
+      ta = mfma64(op, ta[v], ta);
+      tz = mfma64(op, tz[v], tz);
+      if constexpr (v + 1 < RB / 4) {
+        const double a = c < 4 * v + 4 ? 0.0 : -ta[v];
+        ta = mfma64(a, ta[v], ta);
+        tz = mfma64(a, tz[v], tz);
+      }
+    });
+    // T^{-1} = Z^T = (Z' D)^T, and sum over columns c < r of S_cc |Z e_c|^2
+    double q = 0.0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const double zv = tz[v] * sc;
+      sh.tinv[c][4 * v + g] = zv;
+      q += zv * zv;
+    }
+    double tr = c < r ? sh.s[c][c] * q : 0.0;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) tr += __shfl_xor(tr, o);
     if (lane == 0) {
-      sh.bad = bad ? 1 : 0;
-      sh.small = small ? 1 : 0;
+      sh.bad = ok ? 0 : 1;
+      sh.small = sm ? 1 : 0;
       sh.trace = tr;
     }
   }
