@@ -48,6 +48,8 @@ int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 // then leave room for 3 wavefronts per SIMD, so that one block's X, G, R
 // traffic overlaps another block's MFMAs.
 constexpr int kEpiBN = 64;
+constexpr int kFillTiles = 256;   // large tiles when a launch has this many (one per CU),
+constexpr int kLongSlice = 1024;  // or reduction slices at least this long
 
 // Output tile width: 128 unless that wastes more than 10% of the tile.
 int pick_bn(int cols) {
@@ -212,6 +214,29 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     }
     cls_of[i] = c;
     p.cls[c].count++;
+  }
+  // The large split-bfloat16 tiles pay off when a launch has enough of them
+  // to give every CU one, or long reduction slices; with few tiles split
+  // into short slices (a mid-size matrix on its own), the 128-row tiles keep
+  // more CUs busy.  (The update kernel does not split its reduction.)
+  if (p.math) {
+    int64_t big_mv = 0, big_mtu = 0, big_epi = 0;
+    for (const auto& k : p.cls) {
+      if (k.small_rb > 0) continue;
+      if (k.bn_mv == 256) big_mv += static_cast<int64_t>(k.count) * cdiv(k.m, 256) * cdiv(k.r, 256);
+      if (k.bn_mtu == 256) big_mtu += static_cast<int64_t>(k.count) * cdiv(k.n, 256) * cdiv(k.r, 256);
+      if (k.bn_n == 256) big_epi += static_cast<int64_t>(k.count) * cdiv(k.m, 256) * cdiv(k.n, 128);
+    }
+    auto short_slices = [](int64_t tiles, int K) {
+      int sp, kl;
+      pick_split(tiles, K, sp, kl);
+      return kl < kLongSlice;
+    };
+    for (auto& k : p.cls) {
+      if (big_mv < kFillTiles && k.bn_mv == 256 && short_slices(big_mv, k.n)) k.bn_mv = k.bn_r;
+      if (big_mtu < kFillTiles && k.bn_mtu == 256 && short_slices(big_mtu, k.m)) k.bn_mtu = k.bn_r;
+      if (big_epi < kFillTiles && k.bn_n == 256) k.bn_n = kEpiBN;
+    }
   }
   int first = 0;
   for (auto& k : p.cls) {
