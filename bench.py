@@ -313,23 +313,25 @@ OTHER_CONFIGS = (("single-256x128", 1, None, 1000, ((0,), 10), True),
                  ("mlp70b-r2048", 5, 2048, 10, ((0,), 1), False))
 
 
-def time_configs(dion, torch, dev, math: str, cpu: bool = True):
+def time_configs(dion, torch, dev, math: str, cpu: bool = True, only=None, variants=("orth", "dion")):
     """steps/s of both variants on every other workload, with the fraction
     of the whole-step roofline each reaches, and the float64 oracle's
     steps/s on the same workload (all BLAS threads; also one thread for the
-    single matrices)."""
+    single matrices).  only: one workload's label."""
     from workloads import config
     from workloads.device import DeviceMatrix
     out = {}
     blas, threads, cpu_name = _blas_info()
     for label, num, r, steps, (sample, osteps), single in OTHER_CONFIGS:
+        if only is not None and label != only:
+            continue
         wl = config(num, r=r) if r else config(num)
         print(f"[bench] {wl.name}", file=sys.stderr, flush=True)
         mats = [DeviceMatrix(wl, s, dev) for s in wl.mats]
         torch.cuda.synchronize()
         shapes = [(s.m, s.n, s.r) for s in wl.mats]
         eg = 2 if wl.g_dtype == "bf16" else 4
-        for var in ("orth", "dion"):
+        for var in variants:
             sec, _ = time_plan(dion, torch, mats, var, steps, 3, wl.eta, wl.beta, math,
                                phases=False)
             entry = {"workload": wl.name, "steps_per_s": round(1 / sec, 2),
@@ -371,6 +373,9 @@ def main(argv=None) -> int:
     ap.add_argument("--main-only", action="store_true",
                     help="time only the main setting (no other arithmetic or rank fraction; "
                          "for profiling runs)")
+    ap.add_argument("--only", choices=[c[0] for c in OTHER_CONFIGS], default=None,
+                    help="time only this workload of --configs (variant --variant), without "
+                         "the 3B stack: for profiling one workload")
     ap.add_argument("--configs", action="store_true",
                     help="also time both variants on the other workloads (single matrices, "
                          "the 160M stack, the 70B MLP matrix) under \"configs\"")
@@ -399,6 +404,11 @@ def main(argv=None) -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only:
+        res = time_configs(dion, torch, dev, args.math, cpu=not args.no_cpu, only=args.only,
+                           variants=(args.variant,))
+        print(json.dumps({"configs": res}))
+        return 0
 
     wl = config(4, args.rank_div, layers=args.layers)
     print(f"[bench] generating {wl.name}: {wl.count} matrices on the device", file=sys.stderr,

@@ -482,12 +482,18 @@ hipError_t factor(const dion_plan& p, Launch base, int which, hipStream_t st) {
   // caller forms between stages, so its single pass is final.
   base.retry = p.sharded && which == 0 ? 0 : 1;
   base.gate = kGateAll;   // k_chol_init clears the control bits
+  int blocks = 0;
+  for (const ClassRec& c : p.cls) {
+    const int nb = c.rp / kCholNB;
+    if (c.small_rb == 0) blocks += c.count * nb * (nb + 1) / 2;
+  }
+  const int parts = blocks <= kCholInitSplit ? kCholInitParts : 1;
   DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
     const int nb = c.rp / kCholNB;
     ci.splits = which == 0 ? c.s_gp : c.s_gw;
-    ci.tiles = nb * (nb + 1) / 2 * kCholInitParts;
+    ci.tiles = nb * (nb + 1) / 2 * parts;
     return true;
-  }, [&](const Launch& L) { return launch_chol_init(L, st); }));
+  }, [&](const Launch& L) { return launch_chol_init(L, parts, st); }));
   // Every block step in one dataflow launch (k_chol_flow) when its work
   // items, one workgroup per 64 x 64 block of T and of Y, all fit the chip
   // at once (its kernel holds one workgroup per CU); otherwise a launch per

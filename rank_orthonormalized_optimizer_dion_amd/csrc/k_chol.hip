@@ -103,11 +103,13 @@ __device__ __forceinline__ int* flow_flags(const Launch& L, const MatDesc& d) {
 
 // A = the Gram matrix (the sum of its reduction slices' partials, upper
 // triangle, mirrored), rows past r padded with the identity; diag(S) kept
-// aside.  Work item: a quarter (16 rows) of one 64 x 64 upper block; each
-// thread takes 4 elements and issues all their partials' loads before
-// adding them (in slice order).
-constexpr int kInitParts = kCholInitParts;
+// aside.  Work item: one of PARTS row bands of one 64 x 64 upper block (a
+// quarter when the launch has few blocks, so that it still fills the chip);
+// each thread issues the loads of eight slices' partials of its elements
+// before adding them (in slice order).
+template <int PARTS>
 __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
+  constexpr int kInitParts = PARTS;
   MatDesc d;
   ClassInfo ci;
   int local;
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void k_chol_init(Launch L) {
     e[u] = static_cast<int64_t>(min(gi[u], gj[u])) * rp + max(gi[u], gj[u]);
   }
   double acc[PER] = {};
-  constexpr int kSlices = 8;   // slices' loads in flight per element
+  constexpr int kSlices = PER >= 16 ? 1 : 32 / PER;   // slices' loads in flight per element
   for (int s0 = 0; s0 < ci.splits; s0 += kSlices) {
     double v[kSlices][PER];
 #pragma unroll
@@ -936,7 +938,9 @@ hipError_t go_capped(K kernel, const Launch& L, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_chol_init(const Launch& L, hipStream_t st) { return go(k_chol_init, L, st); }
+hipError_t launch_chol_init(const Launch& L, int parts, hipStream_t st) {
+  return parts == kCholInitParts ? go(k_chol_init<kCholInitParts>, L, st) : go(k_chol_init<1>, L, st);
+}
 hipError_t launch_chol_diag(const Launch& L, hipStream_t st) { return go(k_chol_diag, L, st); }
 hipError_t launch_chol_panel(const Launch& L, hipStream_t st) { return go(k_chol_panel, L, st); }
 hipError_t launch_chol_trail(const Launch& L, hipStream_t st) { return go(k_chol_trail, L, st); }

@@ -22,9 +22,11 @@ hipError_t launch_gram8(const Launch& L, hipStream_t st);
 hipError_t launch_trmm(const Launch& L, int bn, bool vec, int math, hipStream_t st);
 hipError_t launch_epi(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st);
 
-// work items per 64 x 64 upper block of k_chol_init
+// work items per 64 x 64 upper block of k_chol_init: kCholInitParts row
+// bands when the launch has at most kCholInitSplit blocks, else one
 constexpr int kCholInitParts = 4;
-hipError_t launch_chol_init(const Launch& L, hipStream_t st);
+constexpr int kCholInitSplit = 1024;
+hipError_t launch_chol_init(const Launch& L, int parts, hipStream_t st);
 hipError_t launch_chol_diag(const Launch& L, hipStream_t st);
 hipError_t launch_chol_panel(const Launch& L, hipStream_t st);
 hipError_t launch_chol_trail(const Launch& L, hipStream_t st);
