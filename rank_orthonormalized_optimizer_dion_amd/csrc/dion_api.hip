@@ -50,6 +50,11 @@ int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 constexpr int kEpiBN = 64;
 constexpr int kFillTiles = 256;   // large tiles when a launch has this many (one per CU),
 constexpr int kLongSlice = 1024;  // or reduction slices at least this long
+constexpr int kWideTiles = 1024;  // 256 x 192 tiles: four per CU at least
+
+// Rows of an M V / M^T U output tile of width bn: 256 for the
+// split-bfloat16 256 x 256 and 256 x 192 tiles, 128 otherwise.
+int big_rows(int bn) { return bn == 256 || bn == 192 ? 256 : 128; }
 
 // Output tile width: 128 unless that wastes more than 10% of the tile.
 int pick_bn(int cols) {
@@ -61,7 +66,7 @@ struct ClassRec {
   int m, n, r, rp;
   int first, count;
   int bn_r, bn_n, bg;
-  int bn_mv;   // M V tile: bn_r, or 256 (256 x 256 split-bfloat16 tiles)
+  int bn_mv;   // M V tile: bn_r, or 256 / 192 (256 x 256 / 256 x 192 split-bfloat16 tiles)
   int bn_mtu;  // M^T U tile, likewise
   int s_mv, kl_mv, s_mtu, kl_mtu, s_gp, kl_gp, s_gw, kl_gw;
   int s_cn, kl_cn;  // Dion column norms: row slices (<= 64, so the slices'
@@ -205,9 +210,12 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
       // Gram than 128-wide tiles).
       // (The sliced Gram always works on 64-wide tiles.)
       k.bg = k.r > 1024 && !p.gram8 ? pick_bn(k.r) : 64;
-      const bool big_r = k.r * 10 >= cdiv(k.r, 256) * 256 * 9;   // <= 10% of 256-wide tiles idle
-      k.bn_mv = p.math && k.m >= 256 && big_r ? 256 : k.bn_r;
-      k.bn_mtu = p.math && k.n >= 256 && big_r ? 256 : k.bn_r;
+      // large split-bfloat16 tiles: 256 wide when at most 10% of them
+      // idle, else one 192-wide column tile for ranks 129 .. 192
+      const bool big_r = k.r * 10 >= cdiv(k.r, 256) * 256 * 9;
+      const int bn_big = big_r ? 256 : k.r > 128 && k.r <= 192 ? 192 : 0;
+      k.bn_mv = p.math && k.m >= 256 && bn_big ? bn_big : k.bn_r;
+      k.bn_mtu = p.math && k.n >= 256 && bn_big ? bn_big : k.bn_r;
       k.small_rb = p.sharded || (variant & DION_SCHED_GROUPED)
                        ? 0 : small_block(k.m, k.n, k.r, k.small_res);
       p.cls.push_back(k);
@@ -218,13 +226,19 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
   // The large split-bfloat16 tiles pay off when a launch has enough of them
   // to give every CU one, or long reduction slices; with few tiles split
   // into short slices (a mid-size matrix on its own), the 128-row tiles keep
-  // more CUs busy.  (The update kernel does not split its reduction.)
+  // more CUs busy.  (The update kernel does not split its reduction.)  The
+  // 256 x 192 tiles replace 128 x 64 ones, six to one: they need kWideTiles
+  // of them in the launch (the 160M stack's 324 take 1.81 ms per step
+  // against 1.70 with the small tiles; the 3B stack's 2,240 at r = 1/16
+  // take M V from 6.4 to 4.7 ms).
   if (p.math) {
-    int64_t big_mv = 0, big_mtu = 0, big_epi = 0;
+    int64_t big_mv = 0, big_mtu = 0, big_epi = 0, wide_mv = 0, wide_mtu = 0;
     for (const auto& k : p.cls) {
       if (k.small_rb > 0) continue;
       if (k.bn_mv == 256) big_mv += static_cast<int64_t>(k.count) * cdiv(k.m, 256) * cdiv(k.r, 256);
       if (k.bn_mtu == 256) big_mtu += static_cast<int64_t>(k.count) * cdiv(k.n, 256) * cdiv(k.r, 256);
+      if (k.bn_mv == 192) wide_mv += static_cast<int64_t>(k.count) * cdiv(k.m, 256);
+      if (k.bn_mtu == 192) wide_mtu += static_cast<int64_t>(k.count) * cdiv(k.n, 256);
       if (k.bn_n == 256) big_epi += static_cast<int64_t>(k.count) * cdiv(k.m, 256) * cdiv(k.n, 128);
     }
     auto short_slices = [](int64_t tiles, int K) {
@@ -235,6 +249,8 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     for (auto& k : p.cls) {
       if (big_mv < kFillTiles && k.bn_mv == 256 && short_slices(big_mv, k.n)) k.bn_mv = k.bn_r;
       if (big_mtu < kFillTiles && k.bn_mtu == 256 && short_slices(big_mtu, k.m)) k.bn_mtu = k.bn_r;
+      if (wide_mv < kWideTiles && k.bn_mv == 192) k.bn_mv = k.bn_r;
+      if (wide_mtu < kWideTiles && k.bn_mtu == 192) k.bn_mtu = k.bn_r;
       if (big_epi < kFillTiles && k.bn_n == 256) k.bn_n = kEpiBN;
     }
   }
@@ -247,10 +263,8 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
   int64_t t_mv = 0, t_mtu = 0, t_gp = 0, t_gw = 0;
   for (auto& k : p.cls) {
     const int nt = cdiv(k.r, k.bg);
-    const int bm_mv = k.bn_mv == 256 ? 256 : 128;
-    t_mv += static_cast<int64_t>(k.count) * cdiv(k.m, bm_mv) * cdiv(k.r, k.bn_mv);
-    const int bm_mtu = k.bn_mtu == 256 ? 256 : 128;
-    t_mtu += static_cast<int64_t>(k.count) * cdiv(k.n, bm_mtu) * cdiv(k.r, k.bn_mtu);
+    t_mv += static_cast<int64_t>(k.count) * cdiv(k.m, big_rows(k.bn_mv)) * cdiv(k.r, k.bn_mv);
+    t_mtu += static_cast<int64_t>(k.count) * cdiv(k.n, big_rows(k.bn_mtu)) * cdiv(k.r, k.bn_mtu);
     t_gp += static_cast<int64_t>(k.count) * nt * (nt + 1) / 2;
   }
   t_gw = t_gp;
@@ -392,8 +406,8 @@ hipError_t gram(const dion_plan& p, Launch base, int which, hipStream_t st) {
     // (the region exists in every sliced-Gram plan: oQ != 0)
     constexpr int64_t kHasRegion = 1;
     auto fused = [&](const ClassRec& c) {
-      return which == 0 ? c.bn_mv == 256 && q_fused_max(kHasRegion, c.s_mv, cdiv(c.m, 256))
-                        : c.bn_mtu == 256 && !p.sharded && q_fused_max(kHasRegion, c.s_mtu, cdiv(c.n, 256));
+      return which == 0 ? c.bn_mv >= 192 && q_fused_max(kHasRegion, c.s_mv, cdiv(c.m, 256))
+                        : c.bn_mtu >= 192 && !p.sharded && q_fused_max(kHasRegion, c.s_mtu, cdiv(c.n, 256));
     };
     auto qsplit = [&](const ClassRec& c, ClassInfo& ci) {
       const int rows = which == 0 ? c.m : c.n;
@@ -632,10 +646,10 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   // P = M V (split-bfloat16: V^T split once into planes, read as whole cells
   // by every tile)
   if (p.math) DION_TRY(split_t(p, base, 0, st));
-  for (int bn : {256, 128, 64}) {
+  for (int bn : {256, 192, 128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_mv != bn) return false;
-      ci.tx = cdiv(c.m, bn == 256 ? 256 : 128);
+      ci.tx = cdiv(c.m, big_rows(bn));
       ci.ty = cdiv(c.r, bn);
       ci.splits = c.s_mv;
       ci.klen = c.kl_mv;
@@ -663,10 +677,10 @@ hipError_t run_step(const dion_plan& p, const MatDesc* dev_table, float eta, flo
   // W = M^T U (split-bfloat16: U^T split once into planes, read as whole
   // cells by every tile)
   if (p.math) DION_TRY(split_t(p, base, 1, st));
-  for (int bn : {256, 128, 64}) {
+  for (int bn : {256, 192, 128, 64}) {
     DION_TRY(grouped(p, base, [&](const ClassRec& c, ClassInfo& ci) {
       if (c.bn_mtu != bn) return false;
-      ci.tx = cdiv(c.n, bn == 256 ? 256 : 128);
+      ci.tx = cdiv(c.n, big_rows(bn));
       ci.ty = cdiv(c.r, bn);
       ci.splits = c.s_mtu;
       ci.klen = c.kl_mtu;

@@ -576,6 +576,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_mv3(Launch L) {
 // split-bfloat16 conversion work per MFMA.
 using WB = WGrid<256, 256, 2, 4>;
 constexpr int kBigThreads = WB::NT;
+// The same products on 256 x 192 tiles (8 wavefronts, 4 x 2, of 64 x 96)
+// for ranks 129 .. 192: one column tile, so each element of M is loaded
+// and split into bfloat16 planes once per product, where 128 x 64 tiles
+// take it three times at r = 192 (M V on the 3B stack at r = 1/16: 4.7 ms
+// against 6.4).
+using WS = WGrid<256, 192, 4, 2>;
 
 template <class W>
 __device__ __forceinline__ void store_tile_w(float* out_, int64_t ld, int r0, int c0, int rmax,
@@ -631,34 +637,33 @@ __device__ __forceinline__ uint32_t* colmax_slot(const Launch& L, const MatDesc&
   return reinterpret_cast<uint32_t*>(L.ws + d.oQ + q_max_off(max(d.m, d.n), d.r)) + tm * q_cols(d.r);
 }
 
-template <typename GT, bool VEC, bool FULL>
+template <class W, typename GT, bool VEC, bool FULL>
 __device__ __forceinline__ void mv3b_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
                                           int s, int tm, int tn, int kbeg, int kend, u32x4* smem) {
   constexpr int BK = 32;
   const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
-  LoadKC<WB::BM, BK, VEC, false, SrcM<GT>, WB::NT> la(sm, d.n, tm * WB::BM, d.m, kend);
+  LoadKC<W::BM, BK, VEC, false, SrcM<GT>, W::NT> la(sm, d.n, tm * W::BM, d.m, kend);
   const u32x4* vt = reinterpret_cast<const u32x4*>(L.ws + d.oH);
-  const LoadDma<WB::BN, BK, WB::NT> lb{vt, vt + static_cast<int64_t>(d.r) * plane_pitch(d.n) / 8, d.r,
-                                       tn * WB::BN, d.r};
-  f32x16 acc[WB::FM][WB::FN];
+  const LoadDma<W::BN, BK, W::NT> lb{vt, vt + static_cast<int64_t>(d.r) * plane_pitch(d.n) / 8, d.r,
+                                      tn * W::BN, d.r};
+  f32x16 acc[W::FM][W::FN];
   zero_acc(acc);
-  pipeline_bf_dma<WB::BM, WB::BN, BK, FULL>(
+  pipeline_bf_dma<W::BM, W::BN, BK, FULL>(
       la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem,
       [&](const u32x4* ah, const u32x4* al, const u32x4* bh, const u32x4* bl) {
-        mma_tile_bf3w<WB, BK>(ah, al, bh, bl, acc);
+        mma_tile_bf3w<W, BK>(ah, al, bh, bl, acc);
       });
   float* out = ci.splits == 1
                    ? reinterpret_cast<float*>(L.ws + d.oP)
                    : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.m * d.r;
-  store_tile_w<WB>(out, d.r, tm * WB::BM, tn * WB::BN, d.m, d.r, acc);
+  store_tile_w<W>(out, d.r, tm * W::BM, tn * W::BN, d.m, d.r, acc);
   if (q_fused_max(d.oQ, ci.splits, ci.tx))
-    store_colmax<WB>(colmax_slot(L, d, tm), tm * WB::BM, tn * WB::BN, d.m, d.r, acc, smem);
+    store_colmax<W>(colmax_slot(L, d, tm), tm * W::BM, tn * W::BN, d.m, d.r, acc, smem);
 }
 
-template <typename GT, bool VEC>
-__global__ __launch_bounds__(kBigThreads) void k_mv3b(Launch L) {
+template <class W, typename GT, bool VEC>
+__device__ __forceinline__ void mv3b_kernel(const Launch& L, u32x4* smem) {
   constexpr int BK = 32;
-  __shared__ u32x4 smem[2 * bf_stage_cells<WB::BM, WB::BN, BK>()];
   MatDesc d;
   ClassInfo ci;
   int local;
@@ -670,41 +675,52 @@ __global__ __launch_bounds__(kBigThreads) void k_mv3b(Launch L) {
   tile_order(local - s * per, ci.tx, ci.ty, tm, tn);
   const int kbeg = s * ci.klen;
   const int kend = min(d.n, kbeg + ci.klen);
-  const bool full = VEC && (tm + 1) * WB::BM <= d.m && (tn + 1) * WB::BN <= d.r &&
+  const bool full = VEC && (tm + 1) * W::BM <= d.m && (tn + 1) * W::BN <= d.r &&
                     (kend - kbeg) % BK == 0;
-  if (full) mv3b_body<GT, VEC, true>(L, d, ci, s, tm, tn, kbeg, kend, smem);
-  else mv3b_body<GT, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+  if (full) mv3b_body<W, GT, VEC, true>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+  else mv3b_body<W, GT, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
 }
 
-// M^T U on the same 256 x 256 tiles (output rows: n, columns: r).
-template <typename GT, bool VEC, bool FULL>
+template <typename GT, bool VEC>
+__global__ __launch_bounds__(kBigThreads) void k_mv3b(Launch L) {
+  __shared__ u32x4 smem[2 * bf_stage_cells<WB::BM, WB::BN, 32>()];
+  mv3b_kernel<WB, GT, VEC>(L, smem);
+}
+
+template <typename GT, bool VEC>
+__global__ __launch_bounds__(WS::NT) void k_mv3s(Launch L) {
+  __shared__ u32x4 smem[2 * bf_stage_cells<WS::BM, WS::BN, 32>()];
+  mv3b_kernel<WS, GT, VEC>(L, smem);
+}
+
+// M^T U on the same tiles (output rows: n, columns: r).
+template <class W, typename GT, bool VEC, bool FULL>
 __device__ __forceinline__ void mtu3b_body(const Launch& L, const MatDesc& d, const ClassInfo& ci,
                                            int s, int tm, int tn, int kbeg, int kend, u32x4* smem) {
   constexpr int BK = 32;
   const SrcM<GT> sm(static_cast<const GT*>(d.G), d.R);
-  LoadXC<WB::BM, BK, VEC, SrcM<GT>, WB::NT> la(sm, d.n, tm * WB::BM, d.n, kend);
+  LoadXC<W::BM, BK, VEC, SrcM<GT>, W::NT> la(sm, d.n, tm * W::BM, d.n, kend);
   const u32x4* ut = reinterpret_cast<const u32x4*>(L.ws + d.oH);
-  const LoadDma<WB::BN, BK, WB::NT> lb{ut, ut + static_cast<int64_t>(d.r) * plane_pitch(d.m) / 8, d.r,
-                                       tn * WB::BN, d.r};
-  f32x16 acc[WB::FM][WB::FN];
+  const LoadDma<W::BN, BK, W::NT> lb{ut, ut + static_cast<int64_t>(d.r) * plane_pitch(d.m) / 8, d.r,
+                                      tn * W::BN, d.r};
+  f32x16 acc[W::FM][W::FN];
   zero_acc(acc);
-  pipeline_bf_dma<WB::BM, WB::BN, BK, FULL>(
+  pipeline_bf_dma<W::BM, W::BN, BK, FULL>(
       la, lb, kbeg, (kend - kbeg + BK - 1) / BK, smem,
       [&](const u32x4* ah, const u32x4* al, const u32x4* bh, const u32x4* bl) {
-        mma_tile_bf3w<WB, BK>(ah, al, bh, bl, acc);
+        mma_tile_bf3w<W, BK>(ah, al, bh, bl, acc);
       });
   float* out = ci.splits == 1
                    ? reinterpret_cast<float*>(L.ws + d.oW)
                    : reinterpret_cast<float*>(L.ws + d.oK) + static_cast<int64_t>(s) * d.n * d.r;
-  store_tile_w<WB>(out, d.r, tm * WB::BM, tn * WB::BN, d.n, d.r, acc);
+  store_tile_w<W>(out, d.r, tm * W::BM, tn * W::BN, d.n, d.r, acc);
   if (q_fused_max(d.oQ, ci.splits, ci.tx))
-    store_colmax<WB>(colmax_slot(L, d, tm), tm * WB::BM, tn * WB::BN, d.n, d.r, acc, smem);
+    store_colmax<W>(colmax_slot(L, d, tm), tm * W::BM, tn * W::BN, d.n, d.r, acc, smem);
 }
 
-template <typename GT, bool VEC>
-__global__ __launch_bounds__(kBigThreads) void k_mtu3b(Launch L) {
+template <class W, typename GT, bool VEC>
+__device__ __forceinline__ void mtu3b_kernel(const Launch& L, u32x4* smem) {
   constexpr int BK = 32;
-  __shared__ u32x4 smem[2 * bf_stage_cells<WB::BM, WB::BN, BK>()];
   MatDesc d;
   ClassInfo ci;
   int local;
@@ -716,10 +732,22 @@ __global__ __launch_bounds__(kBigThreads) void k_mtu3b(Launch L) {
   tile_order(local - s * per, ci.tx, ci.ty, tm, tn);
   const int kbeg = s * ci.klen;
   const int kend = min(d.m, kbeg + ci.klen);
-  const bool full = VEC && (tm + 1) * WB::BM <= d.n && (tn + 1) * WB::BN <= d.r &&
+  const bool full = VEC && (tm + 1) * W::BM <= d.n && (tn + 1) * W::BN <= d.r &&
                     (kend - kbeg) % BK == 0;
-  if (full) mtu3b_body<GT, VEC, true>(L, d, ci, s, tm, tn, kbeg, kend, smem);
-  else mtu3b_body<GT, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+  if (full) mtu3b_body<W, GT, VEC, true>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+  else mtu3b_body<W, GT, VEC, false>(L, d, ci, s, tm, tn, kbeg, kend, smem);
+}
+
+template <typename GT, bool VEC>
+__global__ __launch_bounds__(kBigThreads) void k_mtu3b(Launch L) {
+  __shared__ u32x4 smem[2 * bf_stage_cells<WB::BM, WB::BN, 32>()];
+  mtu3b_kernel<WB, GT, VEC>(L, smem);
+}
+
+template <typename GT, bool VEC>
+__global__ __launch_bounds__(WS::NT) void k_mtu3s(Launch L) {
+  __shared__ u32x4 smem[2 * bf_stage_cells<WS::BM, WS::BN, 32>()];
+  mtu3b_kernel<WS, GT, VEC>(L, smem);
 }
 
 template <typename GT, int BN, bool VEC, bool FULL>
@@ -927,6 +955,12 @@ hipError_t go(K kernel, const Launch& L, hipStream_t st, int threads = kThreads,
   return vec ? DION_PICK(K, uint16_t, 64, true) : DION_PICK(K, uint16_t, 64, false);
 
 hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st) {
+  if (bn == 192) {   // split-bfloat16 only
+    constexpr int T = WS::NT;
+    if (gdtype == 0)
+      return vec ? go(k_mv3s<float, true>, L, st, T) : go(k_mv3s<float, false>, L, st, T);
+    return vec ? go(k_mv3s<uint16_t, true>, L, st, T) : go(k_mv3s<uint16_t, false>, L, st, T);
+  }
   if (bn == 256) {   // split-bfloat16 only
     constexpr int T = kBigThreads;
     if (gdtype == 0)
@@ -937,6 +971,12 @@ hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, int math, hi
 }
 
 hipError_t launch_mtu(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st) {
+  if (bn == 192) {   // split-bfloat16 only
+    constexpr int T = WS::NT;
+    if (gdtype == 0)
+      return vec ? go(k_mtu3s<float, true>, L, st, T) : go(k_mtu3s<float, false>, L, st, T);
+    return vec ? go(k_mtu3s<uint16_t, true>, L, st, T) : go(k_mtu3s<uint16_t, false>, L, st, T);
+  }
   if (bn == 256) {   // split-bfloat16 only
     constexpr int T = kBigThreads;
     if (gdtype == 0)

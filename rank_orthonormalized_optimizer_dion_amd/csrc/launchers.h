@@ -8,7 +8,8 @@ namespace dion {
 
 // gdtype: 0 = float32 G, 1 = bfloat16 G.  bn: output tile width (64 or 128;
 // 256 selects the split-bfloat16 large tiles: 256 x 256 for launch_mv and
-// launch_mtu, 256 x 128 for launch_epi).
+// launch_mtu, 256 x 128 for launch_epi; 192 the split-bfloat16 256 x 192
+// tiles of launch_mv and launch_mtu).
 // vec: every operand of the launch admits 16-byte vector loads.
 // math: 0 = float32 MFMA products, 1 = split-bfloat16 (three bf16 MFMAs).
 hipError_t launch_mv(const Launch& L, int gdtype, int bn, bool vec, int math, hipStream_t st);

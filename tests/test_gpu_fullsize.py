@@ -7,6 +7,8 @@
   every matrix is checked for the step's invariants and for its residual
   R' = beta (M - U W^T) on a sample of rows and columns, formed from its own
   U (read back from the workspace) and full rows and columns of M.
+* A stack of 128 ragged 2100 x 2060 matrices at r = 150, large enough for
+  the 256 x 192 split-bfloat16 product tiles, sampled against the oracle.
 * The 8192 x 28672 matrix at rank 2048 (Orth-Dion), one step against the
   full float64 oracle.
 The long horizons are in test_gpu_horizon.py.
@@ -113,6 +115,69 @@ def test_config4_full_stack(gpu_lib, variant, rank_div):
             assert_close(err, TOL_1, f"config4 matrix {idx} {variant} {arith}")
         plan.close()
         del ws
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("variant", [ORTH, DION])
+@pytest.mark.parametrize("r", [150, 152])
+def test_wide_tiles_ragged_stack(gpu_lib, variant, r):
+    """128 matrices of 2100 x 2060 at r = 150 or 152 in one split-bfloat16
+    grouped step: 1,152 tiles per product launch, so M V and M^T U take the
+    256 x 192 tiles, with every edge ragged (rows past 2100 and 2060,
+    reduction lengths that are not multiples of 32, idle columns past r);
+    r = 152 keeps 16-byte rows (the vector loads), r = 150 does not.
+    Matrices 0, 63 and 127 take the seeded numpy streams and are checked
+    against the float64 oracle; every matrix is checked for the step's
+    invariants."""
+    import torch
+    from workloads import MatrixSpec, Workload
+    from workloads.device import DeviceMatrix
+    m, n, count = 2100, 2060, 128
+    wl = Workload(name="wide-tiles-ragged", seed=77,
+                  mats=tuple(MatrixSpec(i, "W", i, m, n, r) for i in range(count)),
+                  g_dtype="f32", g_kind="normal", noise=(1.0,) * count, planted_rank=0,
+                  eta=0.01, beta=0.95, steps=1, variants=("orth", "dion"))
+    sampled = (0, 63, 127)
+    dev = torch.device("cuda", 0)
+    mats, cases = [], {}
+    for s in wl.mats:
+        if s.index in sampled:
+            c = Case(wl, s)
+            c.load_grad(0)
+            cases[s.index] = c
+            mats.append((c.X, c.G, c.R, c.V))
+        else:
+            d = DeviceMatrix(wl, s, dev)
+            mats.append((d.X, d.G, d.R, d.V))
+    x0 = [t[0].clone() for t in mats]
+    say(f"wide tiles {variant}: one grouped split-bfloat16 step over {count} matrices")
+    plan = gpu_lib.Plan(mats, variant, math="bf16x3")
+    ws = plan.new_workspace()
+    plan.step(wl.eta, wl.beta, ws)
+    rc, per = gpu_lib.status(ws, plan.count)
+    assert rc == 0, per
+    eta = f32(wl.eta)
+    for s, (X, G, R, V), xp in zip(wl.mats, mats, x0):
+        dx = torch.linalg.norm(xp.double() - X.double()).item()
+        assert abs(dx - eta * math.sqrt(r)) < 1e-3 * eta * math.sqrt(r), (s.index, dx)
+        Vd = V.double()
+        if variant == ORTH:
+            err = (Vd.T @ Vd - torch.eye(r, device=Vd.device, dtype=Vd.dtype)).abs().max().item()
+            assert err < 1e-4, (s.index, err)
+        else:
+            err = (torch.linalg.norm(Vd, dim=0) - 1.0).abs().max().item()
+            assert err < 1e-5, (s.index, err)
+    for idx, c in cases.items():
+        say(f"wide tiles {variant}: oracle on matrix {idx}")
+        res, x_prev = c.oracle(variant)
+        X = c.X.double().cpu().numpy()
+        err = {"X": rel_fro(X, res.X), "R": rel_fro(c.R.double().cpu().numpy(), res.R),
+               "V": rel_fro(c.V.double().cpu().numpy(), res.V),
+               "dX": rel_fro(X - x_prev, res.X - x_prev)}
+        say(f"  matrix {idx}: {err}")
+        assert_close(err, TOL_1, f"wide tiles matrix {idx} {variant}")
+    plan.close()
+    del ws
 
 
 @pytest.mark.timeout(400)
