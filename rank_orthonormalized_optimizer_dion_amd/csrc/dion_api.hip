@@ -36,6 +36,10 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kTargetBlocks = 1024;   // split the reduction below this many tiles
+// The same for launches of large split-bfloat16 tiles only, which hold one
+// workgroup per CU: one round of workgroups (the 8192 x 28672 matrix at
+// r = 512 takes 4 slices of M V instead of 16, 248 steps/s against 232).
+constexpr int kTargetBigBlocks = 256;
 constexpr int kMinSplitLen = 256;     // shortest reduction slice worth a split
 constexpr int kBK = 32;
 constexpr int kBlockThreads = 256;  // threads of every libdion workgroup
@@ -150,10 +154,10 @@ bool vec_ok(const dion_matrix& a, int gdtype) {
 
 // Split count and slice length for a reduction of length K when the launch
 // has `tiles` output tiles in total.
-void pick_split(int64_t tiles, int K, int& s, int& klen) {
+void pick_split(int64_t tiles, int K, int& s, int& klen, int target = kTargetBlocks) {
   s = 1;
-  if (tiles < kTargetBlocks / 2) {
-    s = cdiv(kTargetBlocks, tiles);
+  if (tiles < target / 2) {
+    s = cdiv(target, tiles);
     s = std::max(1, std::min(s, K / kMinSplitLen));
   }
   klen = cdiv(cdiv(K, s), kBK) * kBK;
@@ -268,9 +272,15 @@ int build_plan(const dion_matrix* mats, int count, int variant, int gdtype, bool
     t_gp += static_cast<int64_t>(k.count) * nt * (nt + 1) / 2;
   }
   t_gw = t_gp;
+  bool all_big_mv = true, all_big_mtu = true;
+  for (const auto& k : p.cls) {
+    if (k.small_rb > 0) continue;
+    all_big_mv = all_big_mv && k.bn_mv >= 192;
+    all_big_mtu = all_big_mtu && k.bn_mtu >= 192;
+  }
   for (auto& k : p.cls) {
-    pick_split(t_mv, k.n, k.s_mv, k.kl_mv);
-    pick_split(t_mtu, k.m, k.s_mtu, k.kl_mtu);
+    pick_split(t_mv, k.n, k.s_mv, k.kl_mv, all_big_mv ? kTargetBigBlocks : kTargetBlocks);
+    pick_split(t_mtu, k.m, k.s_mtu, k.kl_mtu, all_big_mtu ? kTargetBigBlocks : kTargetBlocks);
     pick_split(t_gp, k.m, k.s_gp, k.kl_gp);
     if (p.sharded) {   // the Gram exchange buffer is one plane of S
       k.s_gp = 1;
