@@ -422,12 +422,16 @@ def main(argv=None) -> int:
                             wl.eta, wl.beta, args.math)
     f, b = phase_model(shapes, args.variant, eg)
     dom = max(phases, key=phases.get)
-    # kernels of each phase on this stack (every class takes the large
-    # split-bfloat16 tiles: rows and ranks are multiples of 256)
+    # kernels of each phase on this stack (split-bfloat16: the 256 x 256
+    # product tiles at r = 1/4, where rows and ranks are multiples of 256;
+    # at r = 1/16 the 256 x 192 tiles of its r = 192 classes, which carry
+    # nearly all of the products)
     names = {"mv": "k_mv", "orth_p": "orth(P)", "mtu": "k_mtu", "right": "right factor",
              "update": "k_epi"}
     if args.math == "bf16x3":
-        names.update(mv="k_mv3b", mtu="k_mtu3b", update="k_epi3b")
+        wide = args.rank_div == 16
+        names.update(mv="k_mv3s" if wide else "k_mv3b", mtu="k_mtu3s" if wide else "k_mtu3b",
+                     update="k_epi3b")
     kernel = names[dom]
     traffic = measured_traffic(kernel, wl.name) if kernel.startswith("k_") else None
     roof = roofline_of(dom, phases[dom], f, b, traffic, args.math)
