@@ -112,3 +112,28 @@ def test_shard_api_errors(gpu_lib):
     sharded.close()
     with pytest.raises(gpu_lib.DionError):
         gpu_lib.step(c.X, c.G, c.R, c.V, wl.eta, wl.beta, gpu_lib.VARIANTS["orth"] | gpu_lib.SHARDED)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("variant", [ORTH, DION])
+def test_sharded_wide_tiles(gpu_lib, variant):
+    # A 4096 x 16500 matrix at r = 152 in 16 row shards of 256: the shards'
+    # M^T U launch has 16 x 65 = 1,040 tiles, enough for the 256 x 192
+    # split-bfloat16 tiles, whose column maxima a sharded plan takes afresh
+    # from the exchanged W.
+    m, n, r = 4096, 16500, 152
+    bounds = tuple(range(0, m + 1, 256))
+    wl, c = _global_case(m, n, r, "bf16", seed=12)
+    say(f"shard wide tiles {m}x{n} r={r} {len(bounds) - 1} shards {variant}")
+    shards = _sharded_step(gpu_lib, c, bounds, variant, "bf16x3", wl.eta, wl.beta)
+    res, x_prev = c.oracle(variant)
+    X = np.concatenate([s[0].double().cpu().numpy() for s in shards])
+    R = np.concatenate([s[2].double().cpu().numpy() for s in shards])
+    errs = {"X": rel_fro(X, res.X), "R": rel_fro(R, res.R),
+            "dX": rel_fro(X - x_prev, res.X - x_prev),
+            "V": rel_fro(shards[0][3].double().cpu().numpy(), res.V)}
+    say(f"  errors {errs}")
+    for k, e in errs.items():
+        assert e <= TOL_1, (k, e)
+    for s in shards[1:]:
+        assert bool((s[3] == shards[0][3]).all())
