@@ -3,7 +3,7 @@ Llama-shaped stack (28 layers, 196 matrices: Q/O 3072x3072, K/V 3072x1024,
 gate/up 3072x8192, down 8192x3072; float32 X, R, V; bfloat16 G) on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant orth]
-                    [--rank-div 4] [--extra] [--configs] [--no-cpu]
+                    [--rank-div 4] [--extra] [--no-configs] [--no-cpu]
 
 One step = one grouped libdion step over all 196 matrices (every phase of
 the method).  Inputs are synthetic, drawn on the device before timing.
@@ -11,7 +11,8 @@ Prints one JSON line.  The per-phase durations come from HIP events the
 library records on its own stream during the timed steps; the dominant
 phase (one kernel launch) is reported against the MI355X roofline.  The
 line also carries the same stack with the other arithmetic of the products
-and at the other rank fraction.  The CPU baseline is the float64 oracle on
+and at the other rank fraction, and both variants on the other workloads
+(with the oracle beside each).  The CPU baseline is the float64 oracle on
 a bounded sample of the same workload (four layers), scaled to the whole
 stack.
 """
@@ -376,9 +377,10 @@ def main(argv=None) -> int:
     ap.add_argument("--only", choices=[c[0] for c in OTHER_CONFIGS], default=None,
                     help="time only this workload of --configs (variant --variant), without "
                          "the 3B stack: for profiling one workload")
-    ap.add_argument("--configs", action="store_true",
-                    help="also time both variants on the other workloads (single matrices, "
-                         "the 160M stack, the 70B MLP matrix) under \"configs\"")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the other workloads (single matrices, the 160M stack, the 70B "
+                         "MLP matrix), which the line otherwise carries under \"configs\" "
+                         "with both variants and their oracle baselines")
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (a known byte "
@@ -515,7 +517,7 @@ def main(argv=None) -> int:
     del mats
     torch.cuda.empty_cache()
     if args.configs:
-        out["configs"] = time_configs(dion, torch, dev, args.math)
+        out["configs"] = time_configs(dion, torch, dev, args.math, cpu=not args.no_cpu)
     if not args.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.variant, args.cpu_layers)
