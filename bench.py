@@ -388,7 +388,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: the Dion step here runs on a single MI355X and "
-              "has no multi-GPU path (how it would shard is described in DESIGN.md).",
+              "has no multi-GPU path (a row-sharded step's per-shard stages are the "
+              "DION_SHARDED plans, with the Gram matrix and W as the exchange points).",
               file=sys.stderr)
         return 2
 
