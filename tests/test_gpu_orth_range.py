@@ -22,8 +22,8 @@ summation order, |C - AB| against |A| |B| (relative Frobenius), at its
 arithmetic's accuracy.  The whole step is not compared with the oracle's
 step on the original inputs here: at these condition numbers the float32
 product M V alone moves the Q factor by about kappa times float32's
-rounding, for any float32 implementation, so only the factorization of the
-factor the library itself formed is compared."""
+rounding, for any float32 implementation, so each stage is compared on the
+library's own inputs to it instead."""
 import numpy as np
 import pytest
 
