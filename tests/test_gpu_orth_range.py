@@ -178,3 +178,25 @@ def test_two_pass_is_deterministic(gpu_lib, arith):
         b = _run(gpu_lib, [case], "orth", arith)[3][0]
         for k in ("X", "R", "V", "U", "W"):
             assert np.array_equal(a[k], b[k]), (side, k)
+
+
+@pytest.mark.parametrize("variant", ["orth", "dion"])
+@pytest.mark.parametrize("arith", ["f32", "bf16x3"])
+def test_ill_conditioned_many_matrices(gpu_lib, variant, arith):
+    # 30 matrices at r = 150 (three 64-blocks a side, 270 blocks of T and
+    # Y in the plan: more than one launch holds at once), mixing well- and
+    # ill-conditioned factors on both sides, in one grouped step: the first
+    # pass, its shifted retry and the second pass of every matrix must each
+    # give the Q factor of the library's own input
+    m, n, r = 300, 260, 150
+    cases, names = [], []
+    for i in range(30):
+        kappa = (10.0, 1e4, 1e6)[i % 3]
+        side = "P" if (i // 3) % 2 == 0 else "W"
+        cases.append(conditioned_inputs(m, n, r, kappa, seed=500 + i, g_dtype="f32", side=side))
+        names.append(f"matrix {i} kappa={kappa:.0e} ({side})")
+    say(f"30 matrices {m}x{n} r={r} {variant} {arith}")
+    rc, per, raw, out = _run(gpu_lib, cases, variant, arith)
+    assert rc == 0, per
+    for case, o, what in zip(cases, out, names):
+        _check_stages(case, o, variant, arith, f"{what} {variant} {arith}")
